@@ -1,0 +1,117 @@
+"""Seeded synthetic inputs shared by the tests, the benchmark and the oracle checks.
+
+This module only draws numbers and rounds them to bfloat16.  It holds none of the
+attention arithmetic (no RoPE, masks, softmax or gating): both the HIP path and the
+CPU oracle receive the same bf16 bit patterns from here and nothing else.
+
+Recipe (every tensor):
+  * i.i.d. N(0, 1) float32 values from numpy's PCG64 generator;
+  * the tensor is cut into blocks of ``BLOCK`` elements in C order; block ``i`` is
+    drawn from ``SeedSequence(seed, spawn_key=(tensor_index, i))`` so the values do
+    not depend on how many threads produce them;
+  * each float32 value is rounded to bfloat16 by round-to-nearest-even on its bits.
+
+Shapes follow the model the pages describe: 16 query heads, 4 KV heads, head_dim 256
+(Spark-X2.6-4B-FP8 walkthrough, nxmr.cn/news/148448, section 一, config table).
+"""
+from __future__ import annotations
+
+import os
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+
+N_Q_HEADS = 16
+N_KV_HEADS = 4
+HEAD_DIM = 256
+BLOCK = 1 << 22
+
+# Seeds of the five workloads and of the 36-layer stack.
+CONFIG_SEED = {1: 20261, 2: 20262, 3: 20263, 4: 20264, 5: 20265}
+
+
+def _threads() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to bfloat16 (nearest, ties to even); returns uint16 bits."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    lsb = (u >> np.uint32(16)) & np.uint32(1)
+    r = (u + np.uint32(0x7FFF) + lsb) >> np.uint32(16)
+    return r.astype(np.uint16)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def normal_bf16(seed: int, tensor_index: int, shape) -> np.ndarray:
+    """N(0,1) bf16 bit patterns of ``shape`` for tensor ``tensor_index`` of a seed."""
+    shape = tuple(int(s) for s in shape)
+    n = int(np.prod(shape)) if shape else 1
+    out = np.empty(n, dtype=np.uint16)
+    nblk = (n + BLOCK - 1) // BLOCK
+
+    def fill(i: int) -> None:
+        lo = i * BLOCK
+        hi = min(n, lo + BLOCK)
+        ss = np.random.SeedSequence(seed, spawn_key=(tensor_index, i))
+        vals = np.random.default_rng(ss).standard_normal(hi - lo, dtype=np.float32)
+        out[lo:hi] = f32_to_bf16_bits(vals)
+
+    if nblk <= 1:
+        for i in range(nblk):
+            fill(i)
+    else:
+        with ThreadPoolExecutor(_threads()) as ex:
+            list(ex.map(fill, range(nblk)))
+    return out.reshape(shape)
+
+
+def prefill_inputs(seed: int, batch: int, seq: int) -> dict:
+    """Q [B,S,16,256], K/V [B,S,4,256], gate logits [B,S,16]; bf16 bits, pre-RoPE."""
+    return {
+        "q": normal_bf16(seed, 0, (batch, seq, N_Q_HEADS, HEAD_DIM)),
+        "k": normal_bf16(seed, 1, (batch, seq, N_KV_HEADS, HEAD_DIM)),
+        "v": normal_bf16(seed, 2, (batch, seq, N_KV_HEADS, HEAD_DIM)),
+        "gate": normal_bf16(seed, 3, (batch, seq, N_Q_HEADS)),
+    }
+
+
+def stack_layer_seed(layer: int) -> int:
+    """Seed of layer ``layer`` (0-based) of the 36-layer prefill stack."""
+    return CONFIG_SEED[4] * 1000 + layer
+
+
+def decode_seq_lens(seed: int, batch: int, lo: int, hi: int) -> np.ndarray:
+    """Per-sequence context lengths drawn uniformly from [lo, hi] (inclusive)."""
+    rng = np.random.default_rng(np.random.SeedSequence(seed, spawn_key=(99,)))
+    return rng.integers(lo, hi + 1, size=batch).astype(np.int32)
+
+
+def cache_rows(seed: int, b: int, n: int) -> tuple:
+    """Cache rows (K, V) [n,4,256] of sequence ``b``: keys are treated as already rotated."""
+    k = normal_bf16(seed, 2 + 2 * b, (n, N_KV_HEADS, HEAD_DIM))
+    v = normal_bf16(seed, 3 + 2 * b, (n, N_KV_HEADS, HEAD_DIM))
+    return k, v
+
+
+def decode_inputs(seed: int, batch: int, capacity: int, fill_lens=None) -> dict:
+    """Query [B,16,256], gate logits [B,16] and a K/V cache [B,capacity,4,256].
+
+    With ``fill_lens`` only the first ``min(fill_lens[b], capacity)`` slots of sequence
+    ``b`` are drawn (by ``cache_rows``); the rest stay zero and are never read.
+    """
+    q = normal_bf16(seed, 0, (batch, N_Q_HEADS, HEAD_DIM))
+    gate = normal_bf16(seed, 1, (batch, N_Q_HEADS))
+    ck = np.zeros((batch, capacity, N_KV_HEADS, HEAD_DIM), dtype=np.uint16)
+    cv = np.zeros_like(ck)
+    for b in range(batch):
+        n = capacity if fill_lens is None else min(int(fill_lens[b]), capacity)
+        ck[b, :n], cv[b, :n] = cache_rows(seed, b, n)
+    return {"q": q, "gate": gate, "cache_k": ck, "cache_v": cv}

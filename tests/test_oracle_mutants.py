@@ -1,0 +1,54 @@
+"""Plant one plausible mistake at a time in a copy of the oracle (on the CPU) and check
+that at least one pin in ``oracle_pins`` fails for it.  This shows the pins are strong
+enough that a dropped term, a wrong sign, an off-by-one window or a wrong head map in
+the oracle would not go unnoticed."""
+import os
+import types
+
+import pytest
+
+import oracle_pins as P
+
+SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle", "attention.py")
+
+MUTANTS = {
+    "window_boundary_off_by_one": ("vis &= (q - k) < int(window)", "vis &= (q - k) <= int(window)"),
+    "causal_excludes_self": ("vis = k <= q", "vis = k < q"),
+    "scale_one_over_d": ("return 1.0 / math.sqrt(head_dim)", "return 1.0 / head_dim"),
+    "gqa_modulo_map": ("return h // (n_q_heads // n_kv_heads)", "return h % n_kv_heads"),
+    "rope_sign_flip": ("y[..., :half] = x1 * c - x2 * s", "y[..., :half] = x1 * c + x2 * s"),
+    "rope_freq_missing_factor_2": ("-2.0 * m / float(rot_dim)", "-1.0 * m / float(rot_dim)"),
+    "rope_pairs_adjacent": ("x2 = x[..., half:rot_dim]", "x2 = x[..., half:rot_dim][..., ::-1]"),
+    "gate_dropped": ("return o * g[:, None]", "return o"),
+    "gate_sign": ("np.exp(-np.asarray(gate_logit", "np.exp(np.asarray(gate_logit"),
+    "ring_modulo": ("position % window", "position % (window - 1)"),
+    "bf16_truncates": ("np.rint(np.ldexp(x, -qexp))", "np.trunc(np.ldexp(x, -qexp))"),
+    "schedule_first_of_group_full": ("layer % 4 == 3", "layer % 4 == 0"),
+    "full_layer_rotates_all_dims": ("return 5000000.0, HEAD_DIM // 4, None", "return 5000000.0, HEAD_DIM, None"),
+    "sliding_theta_wrong": ("return 10000.0, HEAD_DIM, WINDOW", "return 5000000.0, HEAD_DIM, WINDOW"),
+    "decode_query_position": ("qp = L - 1", "qp = L"),
+    "decode_window_short": ("lo = 0 if w is None else max(0, L - w)", "lo = 0 if w is None else max(0, L - w + 1)"),
+    "value_head_fixed": ("vb[:nk, g]", "vb[:nk, 0]"),
+    "append_position_shift": ("p = int(pos[b]) + np.arange(n_new)", "p = int(pos[b]) + 1 + np.arange(n_new)"),
+}
+
+
+def _mutant_module(old, new):
+    src = open(SRC).read()
+    assert src.count(old) == 1, f"mutation site must occur exactly once: {old!r}"
+    mod = types.ModuleType("oracle_mutant")
+    exec(compile(src.replace(old, new), "oracle_mutant", "exec"), mod.__dict__)
+    return mod
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_planted_mistake_is_caught(name):
+    att = _mutant_module(*MUTANTS[name])
+    caught = []
+    for pin in P.ALL_PINS:
+        try:
+            pin(att)
+        except (AssertionError, IndexError, ValueError):
+            caught.append(pin.__name__)
+            break
+    assert caught, f"no pin fails for the planted mistake {name}"
