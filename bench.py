@@ -1,0 +1,181 @@
+#!/usr/bin/env python3
+"""Benchmark of the hybrid GQA attention path on one MI355X.
+
+Step = one prefill of a full-attention layer (batch 1, 8192 tokens, 16 query / 4 KV heads,
+head_dim 256, RoPE theta 5e6 on the first 64 dims, sigmoid head gate): RoPE, masked
+QK^T, online softmax, PV and the gate epilogue all run inside the one prefill kernel.
+``value`` is prefill tokens/s.  The same line carries the decode half of the metric,
+measured on batched decode (batch 64, context lengths uniform in [1024, 32768], full
+layer), as KV GB/s against HBM peak, and the CPU oracle timed on a bounded sample.
+
+Inputs are seeded synthetic bf16 N(0,1) tensors already resident in HBM; timing uses HIP
+events on the stream the kernels are launched on.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attention tokens/s (prefill, % MFMA peak) + decode KV GB/s (% HBM peak)"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def to_dev(bits):
+    import numpy as np
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def time_launches(fn, steps, warmup):
+    """Average ms per call over ``steps`` back-to-back calls, HIP events on the current stream."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(steps):
+        fn()
+    end.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps
+
+
+def bench_prefill(fga, synth, steps, warmup, S=8192):
+    import torch
+    inp = synth.prefill_inputs(synth.CONFIG_SEED[2], 1, S)
+    q, k, v, g = (to_dev(inp[n]) for n in ("q", "k", "v", "gate"))
+    out = torch.empty_like(q)
+    ms = time_launches(lambda: fga.prefill(fga.FULL, q, k, v, g, out=out), steps, warmup)
+    pairs = S * (S + 1) // 2                       # visible (query, key) pairs, causal
+    flops = 4 * 256 * 16 * pairs                   # QK^T + PV, 16 query heads
+    tflops = flops / (ms * 1e-3) / 1e12
+    return {
+        "ms": ms,
+        "tokens_per_s": S / (ms * 1e-3),
+        "flops": flops,
+        "tflops": tflops,
+    }
+
+
+def bench_decode(fga, synth, steps, warmup):
+    import numpy as np
+    import torch
+    seed = synth.CONFIG_SEED[3]
+    B, cap = 64, 32768
+    lens = synth.decode_seq_lens(seed, B, 1024, 32768)
+    q = to_dev(synth.normal_bf16(seed, 0, (B, 16, 256)))
+    gate = to_dev(synth.normal_bf16(seed, 1, (B, 16)))
+    cache = fga.KVCache(fga.FULL, B, cap)
+    for b in range(B):
+        kb, vb = synth.cache_rows(seed, b, int(lens[b]))
+        cache.k[b, :lens[b]] = to_dev(kb)
+        cache.v[b, :lens[b]] = to_dev(vb)
+    sl = torch.as_tensor(lens).cuda()
+    ws = torch.empty(fga.decode_workspace_bytes(fga.FULL, B, cap), dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(q)
+    ms = time_launches(lambda: fga.decode(fga.FULL, q, gate, cache, sl, cap, out=out, workspace=ws),
+                       steps, warmup)
+    kv_bytes = int(lens.astype(np.int64).sum()) * 4 * 256 * 2 * 2
+    io_bytes = B * (16 * 256 * 2 * 2 + 16 * 2)
+    gbs = (kv_bytes + io_bytes) / (ms * 1e-3) / 1e9
+    return {"ms": ms, "bytes": kv_bytes + io_bytes, "gbs": gbs, "lens_sum": int(lens.sum())}
+
+
+def cpu_baseline(synth, budget_s=12.0, S=8192):
+    """The oracle, as it stands, on randomly sampled query rows of the prefill workload."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    inp = synth.prefill_inputs(synth.CONFIG_SEED[2], 1, S)
+    rng = np.random.default_rng(12345)
+    rows_done = 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < budget_s:
+        rows = rng.choice(S, size=16, replace=False)
+        oracle.prefill(inp["q"], inp["k"], inp["v"], inp["gate"], oracle.FULL, rows=rows)
+        rows_done += len(rows)
+    dt = time.perf_counter() - t0
+    return {
+        "value": rows_done / dt,
+        "unit": "tokens/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"{rows_done} uniformly random query rows (all 16 heads) of the full-layer "
+                  f"S={S} prefill, fp64 NumPy, {dt:.1f} s",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--skip-decode", action="store_true")
+    ap.add_argument("--skip-prefill", action="store_true")
+    ap.add_argument("--skip-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the path has no "
+              "multi-GPU mode", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import full_gqa_attention_amd as fga
+    import synth
+
+    assert torch.cuda.is_available(), "bench.py needs the GPU"
+    result = {
+        "metric": METRIC, "value": None, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": None, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "full-attention layer causal prefill, batch 1, seq 8192, 16 Q / 4 KV "
+                               "heads, head_dim 256, RoPE theta 5e6 on the first 64 dims, sigmoid "
+                               "head gate, bf16 N(0,1)",
+                   "batch": 1, "seq_len": 8192, "layer_type": "full"},
+    }
+    if not args.skip_prefill:
+        log("prefill ...")
+        p = bench_prefill(fga, synth, args.steps, args.warmup)
+        result["value"] = p["tokens_per_s"]
+        result["ms_per_step"] = p["ms"]
+        result["roofline"] = {"bound": "mfma", "achieved": p["tflops"], "peak": PEAK_BF16_TFLOPS,
+                              "unit": "TFLOP/s", "frac": p["tflops"] / PEAK_BF16_TFLOPS,
+                              "traffic": None}
+        log(f"prefill {p['ms']:.3f} ms  {p['tflops']:.1f} TFLOP/s")
+    if not args.skip_decode:
+        log("decode ...")
+        d = bench_decode(fga, synth, args.steps, args.warmup)
+        result["decode"] = {
+            "workload": "batched decode, batch 64, context lengths uniform in [1024, 32768], full "
+                        "layer, bf16 KV [ctx, 4, 256]",
+            "value": d["gbs"], "unit": "GB/s", "ms_per_step": d["ms"],
+            "roofline": {"bound": "hbm", "achieved": d["gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": d["gbs"] / PEAK_HBM_GBS, "traffic": None},
+        }
+        log(f"decode {d['ms']:.3f} ms  {d['gbs']:.0f} GB/s")
+    if not args.skip_cpu_baseline:
+        log("cpu baseline (oracle) ...")
+        result["cpu_baseline"] = cpu_baseline(synth)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,144 @@
+// extern "C" entry points declared in include/spark_attn.h: host-side argument checks,
+// then one launch (prefill, append) or two (decode) on the caller's stream.  Every check
+// runs before any HIP call, so a rejected call enqueues nothing and touches no device.
+#include "spark_attn.h"
+#include "spark_device.hpp"
+#include "spark_launch.hpp"
+
+namespace {
+
+constexpr int32_t kMaxBatch = 65535;
+constexpr int32_t kMaxSeq = 1 << 20;   // native context of the model: 1,048,576 positions
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned2(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 1u) == 0; }
+bool valid_type(int32_t lt) { return lt == SPARK_LAYER_SLIDING || lt == SPARK_LAYER_FULL; }
+
+spark_status check_cache(int32_t lt, const spark_kv_cache* c, int32_t batch) {
+  if (!c || !c->k || !c->v) return SPARK_ERR_INVALID_ARG;
+  if (!aligned16(c->k) || !aligned16(c->v)) return SPARK_ERR_INVALID_ARG;
+  if (c->batch != batch || c->capacity < 1) return SPARK_ERR_INVALID_ARG;
+  if (lt == SPARK_LAYER_SLIDING && c->capacity != SPARK_WINDOW) return SPARK_ERR_INVALID_ARG;
+  return SPARK_OK;
+}
+
+spark_status from_hip(hipError_t e) { return e == hipSuccess ? SPARK_OK : SPARK_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int32_t spark_abi_version(void) { return SPARK_ATTN_ABI_VERSION; }
+
+const char* spark_status_string(int32_t s) {
+  switch (s) {
+    case SPARK_OK: return "ok";
+    case SPARK_ERR_INVALID_ARG: return "invalid argument";
+    case SPARK_ERR_UNSUPPORTED: return "unsupported request";
+    case SPARK_ERR_WORKSPACE: return "decode workspace too small";
+    case SPARK_ERR_HIP: return "HIP launch failure";
+    default: return "unknown status";
+  }
+}
+
+spark_status spark_attn_prefill(int32_t layer_type, int32_t batch, int32_t seq_len,
+                                int32_t start_pos, const void* q, const void* k,
+                                const void* v, const void* gate_logits,
+                                const spark_kv_cache* cache, void* out, void* stream) {
+  if (!valid_type(layer_type)) return SPARK_ERR_INVALID_ARG;
+  if (batch < 1 || batch > kMaxBatch || seq_len < 1 || seq_len > kMaxSeq) return SPARK_ERR_INVALID_ARG;
+  if (!q || !k || !v || !gate_logits || !out) return SPARK_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned2(gate_logits))
+    return SPARK_ERR_INVALID_ARG;
+  if (start_pos < 0) return SPARK_ERR_INVALID_ARG;
+  if (start_pos != 0) return SPARK_ERR_UNSUPPORTED;
+  if (cache) {
+    const spark_status cs = check_cache(layer_type, cache, batch);
+    if (cs != SPARK_OK) return cs;
+    if (layer_type == SPARK_LAYER_FULL && cache->capacity < seq_len) return SPARK_ERR_INVALID_ARG;
+  }
+  const int rows = spark::prefill_block_rows();
+  const long long nqb = (seq_len + rows - 1) / rows;
+  if (nqb * batch * SPARK_KV_HEADS > 0x7fffffffLL) return SPARK_ERR_INVALID_ARG;
+
+  spark::PrefillArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.gate = static_cast<const uint16_t*>(gate_logits);
+  a.out = static_cast<uint16_t*>(out);
+  a.cache_k = cache ? static_cast<uint16_t*>(cache->k) : nullptr;
+  a.cache_v = cache ? static_cast<uint16_t*>(cache->v) : nullptr;
+  a.batch = batch;
+  a.seq_len = seq_len;
+  a.cache_cap = cache ? cache->capacity : 0;
+  a.nqb = (int)nqb;
+  return from_hip(spark::launch_prefill(layer_type, a, static_cast<hipStream_t>(stream)));
+}
+
+spark_status spark_kv_append(int32_t layer_type, int32_t batch, int32_t n_new,
+                             const void* k, const void* v, const int32_t* pos,
+                             const spark_kv_cache* cache, void* stream) {
+  if (!valid_type(layer_type)) return SPARK_ERR_INVALID_ARG;
+  if (batch < 1 || batch > kMaxBatch || n_new < 1 || n_new > kMaxSeq) return SPARK_ERR_INVALID_ARG;
+  if (!k || !v || !pos) return SPARK_ERR_INVALID_ARG;
+  if (!aligned16(k) || !aligned16(v) || (reinterpret_cast<uintptr_t>(pos) & 3u)) return SPARK_ERR_INVALID_ARG;
+  const spark_status cs = check_cache(layer_type, cache, batch);
+  if (cs != SPARK_OK) return cs;
+
+  spark::AppendArgs a{};
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.pos = pos;
+  a.cache_k = static_cast<uint16_t*>(cache->k);
+  a.cache_v = static_cast<uint16_t*>(cache->v);
+  a.batch = batch;
+  a.n_new = n_new;
+  a.cache_cap = cache->capacity;
+  return from_hip(spark::launch_append(layer_type, a, static_cast<hipStream_t>(stream)));
+}
+
+size_t spark_attn_decode_workspace_bytes(int32_t layer_type, int32_t batch, int32_t max_seq_len,
+                                         int32_t split_keys) {
+  if (!valid_type(layer_type) || batch < 1 || batch > kMaxBatch || max_seq_len < 1 ||
+      max_seq_len > kMaxSeq || split_keys < 0 || (split_keys % 32) != 0)
+    return 0;
+  return spark::plan_decode(layer_type, batch, max_seq_len, split_keys).total_bytes;
+}
+
+spark_status spark_attn_decode(int32_t layer_type, int32_t batch, const void* q,
+                               const void* gate_logits, const spark_kv_cache* cache,
+                               const int32_t* seq_lens, int32_t max_seq_len,
+                               int32_t split_keys, void* workspace,
+                               size_t workspace_bytes, void* out, void* stream) {
+  if (!valid_type(layer_type)) return SPARK_ERR_INVALID_ARG;
+  if (batch < 1 || batch > kMaxBatch || max_seq_len < 1 || max_seq_len > kMaxSeq) return SPARK_ERR_INVALID_ARG;
+  if (split_keys < 0 || (split_keys % 32) != 0) return SPARK_ERR_INVALID_ARG;
+  if (!q || !gate_logits || !seq_lens || !out || !workspace) return SPARK_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(out) || !aligned2(gate_logits) ||
+      (reinterpret_cast<uintptr_t>(seq_lens) & 3u) || (reinterpret_cast<uintptr_t>(workspace) & 255u))
+    return SPARK_ERR_INVALID_ARG;
+  const spark_status cs = check_cache(layer_type, cache, batch);
+  if (cs != SPARK_OK) return cs;
+  if (layer_type == SPARK_LAYER_FULL && max_seq_len > cache->capacity) return SPARK_ERR_INVALID_ARG;
+  const spark::DecodePlan plan = spark::plan_decode(layer_type, batch, max_seq_len, split_keys);
+  if (workspace_bytes < plan.total_bytes) return SPARK_ERR_WORKSPACE;
+
+  spark::DecodeArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.gate = static_cast<const uint16_t*>(gate_logits);
+  a.cache_k = static_cast<const uint16_t*>(cache->k);
+  a.cache_v = static_cast<const uint16_t*>(cache->v);
+  a.seq_lens = seq_lens;
+  a.ws_o = static_cast<float*>(workspace);
+  a.ws_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                     ((plan.ws_o_bytes + 255) & ~static_cast<size_t>(255)));
+  a.out = static_cast<uint16_t*>(out);
+  a.batch = batch;
+  a.cache_cap = cache->capacity;
+  a.nsplit = plan.nsplit;
+  a.split_keys = plan.split_keys;
+  return from_hip(spark::launch_decode(layer_type, a, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

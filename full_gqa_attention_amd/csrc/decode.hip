@@ -1,0 +1,253 @@
+// Split-KV GQA decode for the hybrid sliding/full layer on gfx950.
+//
+// Decode is bound by streaming the KV cache from HBM (F16 vs Q4 comparison page,
+// hotelren.com/news/5475707, section 二: each generated token re-reads its state), so
+// every cache byte is read exactly once: a workgroup (sequence b, split s) has one wave
+// per KV head, and that wave scores the 4 query heads sharing the head against each key
+// row it loads (GQA, Spark-X2.6-4B-Base explainer, eliteato.com/news/34565, section
+// "配套效率设计").  Per chunk of 32 keys:
+//   * S = Q K^T on v_mfma_f32_16x16x32_bf16 (rows = the 4 query heads, padded to 16),
+//     K rows loaded straight into the B operand (64 contiguous bytes per key per load);
+//   * online softmax in fp32 / log2 domain across the 16 lanes that hold the scores;
+//   * O += P V on the VALU in fp32: V rows are loaded fully coalesced (two 512-byte rows
+//     per instruction), each lane owns 8 dims of one key parity, P comes from LDS.
+// Each split writes (max, sum, unnormalised O) per query head to the workspace; a second
+// kernel merges the splits with log-sum-exp weights and applies the sigmoid head gate.
+// Sliding layers read the 512-slot ring; full layers the contiguous cache.
+#include "spark_device.hpp"
+#include "spark_launch.hpp"
+
+namespace spark {
+namespace {
+
+constexpr int kThreads = 256;   // 4 waves = 4 KV heads
+constexpr int kChunk = 32;      // keys per inner iteration
+constexpr int kSlot = kKvHeads * kHeadDim;   // bf16 per cache slot
+
+template <int LT>
+__device__ __forceinline__ int visible_keys(int L) {
+  return LT == kFull ? L : min(L, kWindow);
+}
+
+template <int LT>
+__global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
+  using T = LayerTraits<LT>;
+  __shared__ double s_inv[T::kRot / 2];
+  __shared__ __attribute__((aligned(16))) float s_p[kKvHeads][kChunk][4];
+  __shared__ __attribute__((aligned(16))) float s_alpha[kKvHeads][4];
+
+  const int split = blockIdx.x;
+  const int b = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int g = tid >> 6;
+  const int L = a.seq_lens[b];
+  const int n = min(visible_keys<LT>(L), a.cache_cap);   // never read past the cache
+  const int ks = split * a.split_keys;
+  if (ks >= n) return;                      // uniform over the workgroup
+  const int ke = min(ks + a.split_keys, n);
+
+  if (tid < T::kRot / 2) s_inv[tid] = rope_inv_rev(tid, T::kRot, log2(T::kTheta));
+  __syncthreads();
+
+  // Q as the A operand: lane l holds head l % 16 (only 0..3 are real), dims 32s + 8(l/16) + j.
+  const int hrow = lane & 15;
+  const int kq = lane >> 4;
+  bf16x8 qa[8];
+  {
+    u32x4 raw[8];
+    if (hrow < kGroup) {
+      const uint16_t* qrow = a.q + ((size_t)b * kQHeads + g * kGroup + hrow) * kHeadDim;
+#pragma unroll
+      for (int s = 0; s < 8; ++s) raw[s] = ld_global16(qrow + 32 * s + 8 * kq);
+      const double p = (double)(L - 1);
+      if (LT == kSliding) {        // chunk s pairs with chunk s + 4 (d + 128)
+#pragma unroll
+        for (int s = 0; s < 4; ++s) rope_rotate_chunks(raw[s], raw[s + 4], p, s_inv, 32 * s + 8 * kq);
+      } else {                     // chunk 0 (d < 32) pairs with chunk 1 (d + 32)
+        rope_rotate_chunks(raw[0], raw[1], p, s_inv, 8 * kq);
+      }
+    } else {
+#pragma unroll
+      for (int s = 0; s < 8; ++s) raw[s] = u32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int s = 0; s < 8; ++s) qa[s] = as_bf16x8(raw[s]);
+  }
+
+  const size_t seq_base = (size_t)b * a.cache_cap * kSlot + (size_t)g * kHeadDim;
+  const uint16_t* kbase = a.cache_k + seq_base;
+  const uint16_t* vbase = a.cache_v + seq_base;
+  const int vpar = lane >> 5;           // key parity this lane accumulates
+  const int vdim = 8 * (lane & 31);     // first of the 8 dims this lane owns
+
+  float m_run[4], l_run[4], acc[4][8];
+#pragma unroll
+  for (int h = 0; h < 4; ++h) {
+    m_run[h] = -1e30f;
+    l_run[h] = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[h][e] = 0.0f;
+  }
+
+  for (int c0 = ks; c0 < ke; c0 += kChunk) {
+    u32x4 kr[2][8];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const int key = c0 + 16 * kb + hrow;
+      const bool ok = key < ke;
+      const uint16_t* src = kbase + (size_t)(ok ? key : ks) * kSlot + 8 * kq;
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const u32x4 x = ld_global16(src + 32 * s);
+        kr[kb][s] = ok ? x : u32x4{0, 0, 0, 0};
+      }
+    }
+    u32x4 vr[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int key = c0 + 2 * i + vpar;
+      const bool ok = key < ke;
+      const u32x4 x = ld_global16(vbase + (size_t)(ok ? key : ks) * kSlot + vdim);
+      vr[i] = ok ? x : u32x4{0, 0, 0, 0};
+    }
+
+    // Scores: lanes 0..15 hold heads 0..3 (element v) for key c0 + 16kb + lane.
+    float t[2][4];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      f32x4 sc = f32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int s = 0; s < 8; ++s) sc = mfma_16x16x32(qa[s], as_bf16x8(kr[kb][s]), sc);
+      const bool ok = c0 + 16 * kb + hrow < ke;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) t[kb][v] = ok ? sc[v] * kScoreScaleLog2 : -INFINITY;
+    }
+    float alpha[4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      float mx = fmaxf(t[0][v], t[1][v]);
+#pragma unroll
+      for (int off = 1; off < 16; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+      const float m_new = fmaxf(m_run[v], mx);
+      alpha[v] = __builtin_amdgcn_exp2f(m_run[v] - m_new);
+      const float p0 = __builtin_amdgcn_exp2f(t[0][v] - m_new);
+      const float p1 = __builtin_amdgcn_exp2f(t[1][v] - m_new);
+      t[0][v] = p0;
+      t[1][v] = p1;
+      float ps = p0 + p1;
+#pragma unroll
+      for (int off = 1; off < 16; off <<= 1) ps += __shfl_xor(ps, off);
+      l_run[v] = l_run[v] * alpha[v] + ps;
+      m_run[v] = m_new;
+    }
+    if (lane < 16) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+        *reinterpret_cast<f32x4*>(&s_p[g][16 * kb + lane][0]) =
+            f32x4{t[kb][0], t[kb][1], t[kb][2], t[kb][3]};
+      if (lane == 0) *reinterpret_cast<f32x4*>(&s_alpha[g][0]) = f32x4{alpha[0], alpha[1], alpha[2], alpha[3]};
+    }
+    __builtin_amdgcn_wave_barrier();
+    const f32x4 al = *reinterpret_cast<const f32x4*>(&s_alpha[g][0]);
+#pragma unroll
+    for (int h = 0; h < 4; ++h)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[h][e] *= al[h];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const f32x4 pp = *reinterpret_cast<const f32x4*>(&s_p[g][2 * i + vpar][0]);
+      float x[8];
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        x[2 * w] = bf16_lo(vr[i][w]);
+        x[2 * w + 1] = bf16_hi(vr[i][w]);
+      }
+#pragma unroll
+      for (int h = 0; h < 4; ++h)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[h][e] += pp[h] * x[e];
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+
+  // Merge the two key parities, then write this split's partial results.
+#pragma unroll
+  for (int h = 0; h < 4; ++h)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[h][e] += __shfl_xor(acc[h][e], 32);
+
+  const size_t head0 = ((size_t)b * a.nsplit + split) * kQHeads + g * kGroup;
+  if (lane < 32) {
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      float* dst = a.ws_o + (head0 + h) * kHeadDim + vdim;
+      *reinterpret_cast<f32x4*>(dst) = f32x4{acc[h][0], acc[h][1], acc[h][2], acc[h][3]};
+      *reinterpret_cast<f32x4*>(dst + 4) = f32x4{acc[h][4], acc[h][5], acc[h][6], acc[h][7]};
+    }
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      a.ws_ml[(head0 + h) * 2] = m_run[h];
+      a.ws_ml[(head0 + h) * 2 + 1] = l_run[h];
+    }
+  }
+}
+
+template <int LT>
+__global__ __launch_bounds__(kHeadDim) void decode_reduce_kernel(DecodeArgs a) {
+  const int b = blockIdx.x / kQHeads;
+  const int h = blockIdx.x % kQHeads;
+  const int d = threadIdx.x;
+  const int n = min(visible_keys<LT>(a.seq_lens[b]), a.cache_cap);
+  const int ns = min((n + a.split_keys - 1) / a.split_keys, a.nsplit);
+  const size_t head0 = (size_t)b * a.nsplit * kQHeads + h;
+  float mx = -1e30f;
+  for (int s = 0; s < ns; ++s) mx = fmaxf(mx, a.ws_ml[(head0 + (size_t)s * kQHeads) * 2]);
+  float den = 0.0f, num = 0.0f;
+  for (int s = 0; s < ns; ++s) {
+    const size_t hs = head0 + (size_t)s * kQHeads;
+    const float w = __builtin_amdgcn_exp2f(a.ws_ml[hs * 2] - mx);
+    den += w * a.ws_ml[hs * 2 + 1];
+    num += w * a.ws_o[hs * kHeadDim + d];
+  }
+  const float gl = bf16_to_f32(a.gate[(size_t)b * kQHeads + h]);
+  const float r = num / den * sigmoidf_fast(gl);
+  a.out[((size_t)b * kQHeads + h) * kHeadDim + d] = (uint16_t)(pack_bf16x2(r, 0.0f) & 0xffffu);
+}
+
+}  // namespace
+
+DecodePlan plan_decode(int layer_type, int batch, int max_seq_len, int split_keys) {
+  DecodePlan p{};
+  const int n = layer_type == kFull ? max_seq_len : (max_seq_len < kWindow ? max_seq_len : kWindow);
+  int sk = split_keys;
+  if (sk <= 0) {
+    // Aim for >= 2048 workgroups (8 per CU) without splits shorter than 256 keys.
+    sk = 4096;
+    while (sk > 256 && (long long)batch * ((n + sk - 1) / sk) < 2048) sk >>= 1;
+    if (layer_type == kSliding) sk = 128;
+  }
+  p.split_keys = sk;
+  p.nsplit = (n + sk - 1) / sk;
+  p.ws_o_bytes = (size_t)batch * p.nsplit * kQHeads * kHeadDim * sizeof(float);
+  p.ws_ml_bytes = (size_t)batch * p.nsplit * kQHeads * 2 * sizeof(float);
+  p.total_bytes = ((p.ws_o_bytes + 255) & ~(size_t)255) + p.ws_ml_bytes;
+  return p;
+}
+
+hipError_t launch_decode(int layer_type, const DecodeArgs& a, hipStream_t stream) {
+  const dim3 grid_split(a.nsplit, a.batch);
+  const dim3 grid_reduce(a.batch * kQHeads);
+  if (layer_type == kSliding) {
+    hipLaunchKernelGGL(decode_split_kernel<kSliding>, grid_split, dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL(decode_reduce_kernel<kSliding>, grid_reduce, dim3(kHeadDim), 0, stream, a);
+  } else {
+    hipLaunchKernelGGL(decode_split_kernel<kFull>, grid_split, dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL(decode_reduce_kernel<kFull>, grid_reduce, dim3(kHeadDim), 0, stream, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace spark

@@ -1,0 +1,155 @@
+/*
+ * spark_attn.h -- C ABI of the hybrid sliding/full GQA attention path on AMD Instinct
+ * MI355X (gfx950).
+ *
+ * The model (Spark-X2.5/X2.6-4B family) stacks 36 attention layers: three sliding-window
+ * layers, then one full-attention layer, nine times over, so the last layer is full
+ * (Spark-X2.6-4B-Base hybrid attention explainer, eliteato.com/news/34565, section
+ * "36 层混合注意力排布").  Every layer has 16 query heads over 4 KV heads of dimension 256
+ * (same page, section "配套效率设计"; Spark-X2.6-4B-FP8 walkthrough, nxmr.cn/news/148448,
+ * section 一, config table).
+ *
+ *   layer type | RoPE theta | rotated dims      | keys visible to query i
+ *   -----------+------------+-------------------+-------------------------
+ *   SLIDING    | 1e4        | all 256           | i-512 < j <= i
+ *   FULL       | 5e6        | first 64 (of 256) | j <= i
+ *
+ * (explainer page, sections "滑动窗口 512" and "全局注意力 5M 基频 RoPE" with its
+ * parameter table).  RoPE pairs element m with element m + r/2 of the rotated slice of
+ * width r, angle p * theta^(-2m/r).  Scores are scaled by 1/16 = 1/sqrt(256), the
+ * softmax runs in fp32 (Spark X2.5-4B F16 vs Q4 comparison, hotelren.com/news/5475707,
+ * section 三) and each head's output is multiplied by sigmoid(gate logit) of that head
+ * and token (same section; explainer page, section "配套效率设计").  Query head h reads
+ * KV head h / 4.
+ *
+ * Conventions of every call
+ *  - All tensors are bf16, row-major, innermost dimension contiguous, in device memory
+ *    the caller owns (allocated e.g. through PyTorch).  The library allocates nothing and
+ *    keeps no state between calls; calls on disjoint buffers may run concurrently.
+ *  - Every pointer to a bf16 tensor must be 16-byte aligned.
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and outputs are
+ *    valid once that stream has reached the work.  Nothing synchronises the host.
+ *  - Host-side argument checks run before anything is enqueued; on failure nothing is
+ *    enqueued and the status says why.  Values that live in device memory (`pos`,
+ *    `seq_lens`) cannot be checked: out-of-range values are undefined behaviour.
+ *  - SPARK_ERR_HIP reports a failed launch (hipGetLastError after the launch).
+ */
+#ifndef SPARK_ATTN_H
+#define SPARK_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SPARK_ATTN_ABI_VERSION 1
+
+enum { SPARK_Q_HEADS = 16, SPARK_KV_HEADS = 4, SPARK_HEAD_DIM = 256, SPARK_WINDOW = 512 };
+
+typedef enum spark_layer_type {
+  SPARK_LAYER_SLIDING = 0,
+  SPARK_LAYER_FULL = 1
+} spark_layer_type;
+
+typedef enum spark_status {
+  SPARK_OK = 0,
+  SPARK_ERR_INVALID_ARG = 1, /* null pointer, bad enum, size out of range, misaligned */
+  SPARK_ERR_UNSUPPORTED = 2, /* a valid request this build does not implement        */
+  SPARK_ERR_WORKSPACE = 3,   /* decode workspace smaller than required               */
+  SPARK_ERR_HIP = 4          /* the HIP runtime reported a launch failure            */
+} spark_status;
+
+/*
+ * KV cache of one layer, for `batch` sequences.  The keys are stored after RoPE, the
+ * values as given, both bf16 [batch, capacity, 4, 256].
+ *  - FULL layer: contiguous; position p of a sequence lives in slot p (p < capacity).
+ *    4 KB per token per layer (F16 vs Q4 comparison page, section 一).
+ *  - SLIDING layer: a ring of capacity == 512 slots; position p lives in slot p mod 512,
+ *    so a new token replaces exactly the key that just left the window, and the layer's
+ *    footprint stays 2 MiB per sequence whatever the context (Sharp-Spark-X2.5-4B-GGUF
+ *    guide, mpbf.cn/news/67460, section 三).
+ */
+typedef struct spark_kv_cache {
+  void* k;
+  void* v;
+  int32_t batch;
+  int32_t capacity;
+} spark_kv_cache;
+
+/*
+ * Prefill: attention of `seq_len` new tokens per sequence over themselves, one layer.
+ *   q            bf16 [batch, seq_len, 16, 256], before RoPE
+ *   k, v         bf16 [batch, seq_len, 4, 256], k before RoPE
+ *   gate_logits  bf16 [batch, seq_len, 16]
+ *   out          bf16 [batch, seq_len, 16, 256] (written)
+ *   cache        optional (NULL = none): receives the rotated keys and the values of
+ *                positions 0..seq_len-1 (SLIDING: only the last 512 of them, in their
+ *                ring slots).  cache->batch must equal batch; FULL needs
+ *                capacity >= seq_len.
+ *   start_pos    position of the first token; this build supports 0 only
+ *                (SPARK_ERR_UNSUPPORTED otherwise).
+ * Token t of a sequence sits at position start_pos + t.  1 <= seq_len <= 2^20,
+ * 1 <= batch <= 65535.
+ */
+spark_status spark_attn_prefill(int32_t layer_type, int32_t batch, int32_t seq_len,
+                                int32_t start_pos, const void* q, const void* k,
+                                const void* v, const void* gate_logits,
+                                const spark_kv_cache* cache, void* out, void* stream);
+
+/*
+ * Append `n_new` tokens per sequence to a layer's cache.
+ *   k, v   bf16 [batch, n_new, 4, 256], k before RoPE
+ *   pos    device int32 [batch]: position of the first new token of each sequence
+ * Token t of sequence b is rotated at position pos[b] + t and stored in slot
+ * pos[b] + t (FULL; must be < capacity) or (pos[b] + t) mod 512 (SLIDING; when n_new
+ * exceeds 512 only the last 512 tokens are written, as a sequential append would leave
+ * them).  The caller tracks lengths: afterwards a sequence holds pos[b] + n_new tokens.
+ */
+spark_status spark_kv_append(int32_t layer_type, int32_t batch, int32_t n_new,
+                             const void* k, const void* v, const int32_t* pos,
+                             const spark_kv_cache* cache, void* stream);
+
+/*
+ * Bytes of device workspace spark_attn_decode needs for this shape and split size
+ * (split_keys = 0 lets the library choose, exactly as spark_attn_decode will).
+ * Returns 0 for arguments spark_attn_decode would reject.
+ */
+size_t spark_attn_decode_workspace_bytes(int32_t layer_type, int32_t batch,
+                                         int32_t max_seq_len, int32_t split_keys);
+
+/*
+ * Decode: one query token per sequence against the layer's cache.
+ *   q            bf16 [batch, 16, 256], before RoPE; it is rotated at position L-1
+ *   gate_logits  bf16 [batch, 16]
+ *   cache        the layer's cache, already holding the current token
+ *   seq_lens     device int32 [batch]: L = tokens in the cache including the current one,
+ *                1 <= L <= max_seq_len
+ *   max_seq_len  host upper bound of seq_lens (plans the split of the key sequence);
+ *                FULL: <= capacity
+ *   split_keys   keys per split (multiple of 64), or 0 for the library's choice
+ *   workspace    device scratch of at least spark_attn_decode_workspace_bytes(...)
+ *                bytes, 256-byte aligned, used only during the call
+ *   out          bf16 [batch, 16, 256] (written)
+ * FULL layers read positions 0..L-1; SLIDING layers read positions max(0, L-512)..L-1
+ * from the ring.  Two launches: split attention with per-split partial results, then a
+ * log-sum-exp reduction that also applies the gate.
+ */
+spark_status spark_attn_decode(int32_t layer_type, int32_t batch, const void* q,
+                               const void* gate_logits, const spark_kv_cache* cache,
+                               const int32_t* seq_lens, int32_t max_seq_len,
+                               int32_t split_keys, void* workspace,
+                               size_t workspace_bytes, void* out, void* stream);
+
+/* Static description of a status code; never NULL. */
+const char* spark_status_string(int32_t status);
+
+/* SPARK_ATTN_ABI_VERSION of the built library. */
+int32_t spark_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPARK_ATTN_H */

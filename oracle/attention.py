@@ -260,12 +260,13 @@ def decode(q, gate, cache_k, cache_v, seq_lens, layer_type) -> np.ndarray:
         lo = 0 if w is None else max(0, L - w)
         kpos = np.arange(lo, L)
         slots = np.array([cache_slot(int(p), layer_type) for p in kpos], dtype=np.int64)
-        kr = bf16_to_f64(np.asarray(cache_k)[b, slots])              # [n, Hk, D]
-        vb = bf16_to_f64(np.asarray(cache_v)[b, slots])
         vis = visibility([qp], kpos, w)
         qr = rope(bf16_to_f64(q[b])[None], [qp], th, rd)[0]          # [H, D]
         gb = bf16_to_f64(np.asarray(gate)[b])
-        for h in range(H):
-            g = kv_head_of(h, H, Hk)
-            out[b, h] = _attend(qr[h][None], kr[:, g], vb[:, g], vis, gb[h:h + 1], scale)[0]
+        for g in range(Hk):                                          # one KV head at a time
+            kr = bf16_to_f64(np.asarray(cache_k)[b, slots, g])       # [n, D], already rotated
+            vb = bf16_to_f64(np.asarray(cache_v)[b, slots, g])
+            for h in range(H):
+                if kv_head_of(h, H, Hk) == g:
+                    out[b, h] = _attend(qr[h][None], kr, vb, vis, gb[h:h + 1], scale)[0]
     return out

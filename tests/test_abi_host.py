@@ -1,0 +1,85 @@
+"""The C-ABI library on the CPU: it loads, exports every function the header declares,
+and its host-side argument checks reject bad calls before any HIP call is made."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "spark_attn.h")
+
+fga = pytest.importorskip("full_gqa_attention_amd")
+lib = fga._lib
+
+FAKE = ctypes.c_void_p(0x10000)          # aligned, never dereferenced by rejected calls
+MISALIGNED = ctypes.c_void_p(0x10008)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(spark_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_exports_every_declared_function():
+    names = declared_functions()
+    assert set(names) == set(fga.EXPORTED)
+    for n in names:
+        assert hasattr(lib, n), f"{n} not exported by {fga.LIBRARY_PATH}"
+
+
+def test_version_and_status_strings():
+    assert fga.abi_version() == 1
+    assert fga.status_string(0) == "ok"
+    assert fga.status_string(3) == "decode workspace too small"
+    assert fga.status_string(99) == "unknown status"
+
+
+def _cache(k=FAKE, v=FAKE, batch=1, cap=512):
+    return ctypes.pointer(fga.KvCacheDesc(k.value if k else None, v.value if v else None, batch, cap))
+
+
+def prefill(**kw):
+    a = dict(lt=1, B=1, S=16, start=0, q=FAKE, k=FAKE, v=FAKE, g=FAKE, cache=None, out=FAKE)
+    a.update(kw)
+    return lib.spark_attn_prefill(a["lt"], a["B"], a["S"], a["start"], a["q"], a["k"], a["v"], a["g"],
+                                  a["cache"], a["out"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(lt=2), 1), (dict(lt=-1), 1), (dict(B=0), 1), (dict(S=0), 1), (dict(S=(1 << 20) + 1), 1),
+    (dict(q=None), 1), (dict(out=None), 1), (dict(k=MISALIGNED), 1), (dict(start=-1), 1),
+    (dict(start=5), 2),
+    (dict(lt=0, cache=_cache(cap=511)), 1), (dict(lt=1, cache=_cache(cap=15)), 1),
+    (dict(cache=_cache(batch=2)), 1), (dict(cache=_cache(k=None)), 1),
+])
+def test_prefill_rejects(kw, status):
+    assert prefill(**kw) == status
+
+
+def test_append_rejects():
+    f = lib.spark_kv_append
+    assert f(3, 1, 1, FAKE, FAKE, FAKE, _cache(), None) == 1
+    assert f(0, 1, 0, FAKE, FAKE, FAKE, _cache(), None) == 1
+    assert f(0, 1, 1, FAKE, FAKE, None, _cache(), None) == 1
+    assert f(0, 1, 1, FAKE, FAKE, FAKE, _cache(cap=1024), None) == 1
+    assert f(1, 1, 1, FAKE, FAKE, FAKE, None, None) == 1
+
+
+def test_workspace_planning():
+    ws = fga.decode_workspace_bytes
+    assert ws(1, 64, 32768) > 0
+    assert ws(1, 1, 64, 32) == 2 * 16 * 256 * 4 + 2 * 16 * 2 * 4
+    assert ws(0, 1, 100000, 32) == 16 * 16 * 256 * 4 + 16 * 16 * 2 * 4   # ring: <= 512 keys
+    assert ws(1, 1, 64, 33) == 0 and ws(2, 1, 64) == 0 and ws(1, 0, 64) == 0
+
+
+def test_decode_rejects():
+    f = lib.spark_attn_decode
+    big = 1 << 30
+    assert f(1, 1, FAKE, FAKE, _cache(cap=64), FAKE, 65, 0, FAKE, big, FAKE, None) == 1   # > capacity
+    assert f(1, 1, FAKE, FAKE, _cache(cap=64), FAKE, 64, 48, FAKE, big, FAKE, None) == 1  # split % 32
+    assert f(1, 1, FAKE, FAKE, _cache(cap=64), FAKE, 64, 32, FAKE, 16, FAKE, None) == 3   # workspace
+    assert f(1, 1, FAKE, FAKE, _cache(cap=64), FAKE, 64, 0, MISALIGNED, big, FAKE, None) == 1
+    assert f(0, 1, FAKE, FAKE, _cache(cap=1024), FAKE, 64, 0, FAKE, big, FAKE, None) == 1

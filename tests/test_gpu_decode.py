@@ -1,0 +1,179 @@
+"""Decode and KV-append parity: the HIP path through the C ABI against the fp64 oracle."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from gpu_util import assert_cached_keys_close, assert_parity, bits_of, f64_of, i32_dev, note, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def fga():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import full_gqa_attention_amd as m
+    return m
+
+
+def _ring_from_contiguous(ck, cv, lens):
+    """Ring caches holding positions max(0, L-512)..L-1 of contiguous caches, in slot p mod 512."""
+    B = ck.shape[0]
+    rk = np.zeros((B, 512, 4, 256), np.uint16)
+    rv = np.zeros_like(rk)
+    for b in range(B):
+        L = int(lens[b])
+        p = np.arange(max(0, L - 512), L)
+        rk[b, p % 512] = ck[b, p]
+        rv[b, p % 512] = cv[b, p]
+    return rk, rv
+
+
+def _decode_dev(fga, lt, d, ck, cv, lens, split_keys=0, max_len=None):
+    import torch
+    B = len(lens)
+    cap = ck.shape[1]
+    cache = fga.KVCache(lt, B, cap, k=to_dev(ck), v=to_dev(cv))
+    out = fga.decode(lt, to_dev(d["q"]), to_dev(d["gate"]), cache, i32_dev(lens),
+                     int(max(lens)) if max_len is None else max_len, split_keys=split_keys)
+    torch.cuda.synchronize()
+    return f64_of(out)
+
+
+EDGE = [[1], [5], [511], [512], [513], [1, 37, 600, 1025], [4097, 64, 2000]]
+
+
+@pytest.mark.parametrize("lens", EDGE, ids=["L" + "-".join(map(str, x)) for x in EDGE])
+@pytest.mark.parametrize("split_keys", [0, 32, 96, 4096])
+def test_decode_edges_both_types(fga, lens, split_keys):
+    lens = np.array(lens, np.int32)
+    B, cap = len(lens), int(lens.max())
+    d = synth.decode_inputs(4000 + int(lens.sum()), B, cap, fill_lens=lens)
+    note(f"decode edges lens={lens.tolist()} split={split_keys}")
+    got = _decode_dev(fga, oracle.FULL, d, d["cache_k"], d["cache_v"], lens, split_keys)
+    want = oracle.decode(d["q"], d["gate"], d["cache_k"], d["cache_v"], lens, oracle.FULL)
+    assert_parity(got, want, f"decode full lens={lens.tolist()} split={split_keys}")
+    if split_keys in (0, 32, 96):
+        rk, rv = _ring_from_contiguous(d["cache_k"], d["cache_v"], lens)
+        got = _decode_dev(fga, oracle.SLIDING, d, rk, rv, lens, split_keys)
+        want = oracle.decode(d["q"], d["gate"], rk, rv, lens, oracle.SLIDING)
+        assert_parity(got, want, f"decode sliding lens={lens.tolist()} split={split_keys}")
+
+
+def test_split_count_does_not_change_result(fga):
+    lens = np.array([3000, 1500], np.int32)
+    d = synth.decode_inputs(4100, 2, 3000, fill_lens=lens)
+    outs = [_decode_dev(fga, oracle.FULL, d, d["cache_k"], d["cache_v"], lens, sk) for sk in (32, 256, 2048, 4096)]
+    for o in outs[1:]:
+        assert np.max(np.abs(o - outs[0])) < 4e-3
+
+
+def test_config3_batched_decode(fga):
+    """Batch 64, context lengths uniform in [1024, 32768]; full cache and 512-slot ring."""
+    import torch
+    seed = synth.CONFIG_SEED[3]
+    B, cap = 64, 32768
+    lens = synth.decode_seq_lens(seed, B, 1024, 32768)
+    note(f"config3 lens sum={int(lens.sum())}")
+    q = synth.normal_bf16(seed, 0, (B, 16, 256))
+    gate = synth.normal_bf16(seed, 1, (B, 16))
+    cache = fga.KVCache(oracle.FULL, B, cap)
+    host_k = np.zeros((B, cap, 4, 256), np.uint16)
+    host_v = np.zeros_like(host_k)
+    for b in range(B):
+        kb, vb = synth.cache_rows(seed, b, int(lens[b]))
+        host_k[b, :lens[b]], host_v[b, :lens[b]] = kb, vb
+        cache.k[b, :lens[b]] = to_dev(kb)
+        cache.v[b, :lens[b]] = to_dev(vb)
+    out = fga.decode(oracle.FULL, to_dev(q), to_dev(gate), cache, i32_dev(lens), cap)
+    torch.cuda.synchronize()
+    want = oracle.decode(q, gate, host_k, host_v, lens, oracle.FULL)
+    assert_parity(f64_of(out), want, "config3 full")
+    rk, rv = _ring_from_contiguous(host_k, host_v, lens)
+    del cache
+    ring = fga.KVCache(oracle.SLIDING, B, 512, k=to_dev(rk), v=to_dev(rv))
+    out = fga.decode(oracle.SLIDING, to_dev(q), to_dev(gate), ring, i32_dev(lens), cap)
+    torch.cuda.synchronize()
+    want = oracle.decode(q, gate, rk, rv, lens, oracle.SLIDING)
+    assert_parity(f64_of(out), want, "config3 sliding")
+
+
+@pytest.mark.parametrize("B,L", [(4, 131072), (1, 1048576)], ids=["B4_L131072", "B1_L1048576"])
+def test_config5_long_decode(fga, B, L):
+    """Long-context decode on a full layer (cache capacity = L) and on the sliding ring."""
+    import torch
+    seed = synth.CONFIG_SEED[5] + B
+    lens = np.full(B, L, np.int32)
+    q = synth.normal_bf16(seed, 0, (B, 16, 256))
+    gate = synth.normal_bf16(seed, 1, (B, 16))
+    cache = fga.KVCache(oracle.FULL, B, L)
+    host_k = np.zeros((B, L, 4, 256), np.uint16)
+    host_v = np.zeros_like(host_k)
+    for b in range(B):
+        host_k[b], host_v[b] = synth.cache_rows(seed, b, L)
+        cache.k[b] = to_dev(host_k[b])
+        cache.v[b] = to_dev(host_v[b])
+    note(f"config5 B={B} L={L} uploaded")
+    out = fga.decode(oracle.FULL, to_dev(q), to_dev(gate), cache, i32_dev(lens), L)
+    torch.cuda.synchronize()
+    want = oracle.decode(q, gate, host_k, host_v, lens, oracle.FULL)
+    assert_parity(f64_of(out), want, f"config5 full B={B} L={L}")
+    rk, rv = _ring_from_contiguous(host_k, host_v, lens)
+    del cache
+    ring = fga.KVCache(oracle.SLIDING, B, 512, k=to_dev(rk), v=to_dev(rv))
+    out = fga.decode(oracle.SLIDING, to_dev(q), to_dev(gate), ring, i32_dev(lens), L)
+    torch.cuda.synchronize()
+    want = oracle.decode(q, gate, rk, rv, lens, oracle.SLIDING)
+    assert_parity(f64_of(out), want, f"config5 sliding B={B} L={L}")
+
+
+APPEND = [(oracle.FULL, 1, [0, 7]), (oracle.FULL, 33, [0, 100]), (oracle.SLIDING, 5, [0, 1000]),
+          (oracle.SLIDING, 600, [100, 0]), (oracle.SLIDING, 512, [3, 512])]
+
+
+@pytest.mark.parametrize("lt,n_new,pos", APPEND, ids=[f"lt{a}_n{b}_p{c[0]}" for a, b, c in APPEND])
+def test_kv_append(fga, lt, n_new, pos):
+    import torch
+    B = len(pos)
+    cap = 512 if lt == oracle.SLIDING else max(pos) + n_new + 3
+    ck0 = synth.normal_bf16(4200 + n_new, 0, (B, cap, 4, 256))
+    cv0 = synth.normal_bf16(4200 + n_new, 1, (B, cap, 4, 256))
+    k = synth.normal_bf16(4200 + n_new, 2, (B, n_new, 4, 256))
+    v = synth.normal_bf16(4200 + n_new, 3, (B, n_new, 4, 256))
+    cache = fga.KVCache(lt, B, cap, k=to_dev(ck0), v=to_dev(cv0))
+    fga.kv_append(lt, to_dev(k), to_dev(v), i32_dev(pos), cache)
+    torch.cuda.synchronize()
+    ck, cv = oracle.kv_append(ck0, cv0, k, v, np.array(pos), lt)
+    gv = bits_of(cache.v)
+    assert np.array_equal(gv, cv), f"values/untouched slots differ at {np.argwhere(gv != cv)[:5].tolist()}"
+    assert_cached_keys_close(bits_of(cache.k), ck, f"append lt={lt} n={n_new} pos={pos}")
+
+
+@pytest.mark.parametrize("lt", [oracle.SLIDING, oracle.FULL], ids=["sliding", "full"])
+def test_prefill_then_decode_consistency(fga, lt):
+    """Prefill S tokens into the cache, append token S, decode it: equals oracle prefill row S."""
+    import torch
+    S = 777
+    inp = synth.prefill_inputs(4300, 1, S + 1)
+    cap = 512 if lt == oracle.SLIDING else S + 1
+    cache = fga.KVCache(lt, 1, cap)
+    pre = {n: inp[n][:, :S] for n in inp}
+    fga.prefill(lt, to_dev(pre["q"]), to_dev(pre["k"]), to_dev(pre["v"]), to_dev(pre["gate"]), cache=cache)
+    fga.kv_append(lt, to_dev(inp["k"][:, S:]), to_dev(inp["v"][:, S:]), i32_dev([S]), cache)
+    out = fga.decode(lt, to_dev(inp["q"][:, S]), to_dev(inp["gate"][:, S]), cache, i32_dev([S + 1]), S + 1)
+    torch.cuda.synchronize()
+    want = oracle.prefill(inp["q"], inp["k"], inp["v"], inp["gate"], lt, rows=[S])[:, 0]
+    assert_parity(f64_of(out), want, f"prefill->append->decode lt={lt}")
+
+
+def test_decode_rejects_small_workspace(fga):
+    import torch
+    cache = fga.KVCache(oracle.FULL, 1, 64)
+    q = torch.zeros(1, 16, 256, dtype=torch.bfloat16, device="cuda")
+    g = torch.zeros(1, 16, dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(256, dtype=torch.uint8, device="cuda")
+    with pytest.raises(fga.SparkError) as e:
+        fga.decode(oracle.FULL, q, g, cache, i32_dev([64]), 64, workspace=ws, split_keys=32)
+    assert e.value.status == 3
