@@ -1,305 +1,431 @@
 // Flash-attention prefill for the hybrid sliding/full GQA layer on gfx950.
 //
-// One workgroup = 8 waves = one KV head g of one sequence and a block of 64 query
-// positions; wave w computes query head 4g + w/2 for 32 of those positions, so every K/V
-// tile staged in LDS serves 4 query heads x 64 positions = 256 query rows (GQA sharing).
+// One workgroup = 4 waves (one per SIMD) = one KV head g of one sequence and a block of
+// 64 query positions; wave w computes query head 4g + w for all 64 positions as two
+// 32-row blocks.  Every K/V tile in LDS thus serves 4 query heads x 64 positions (GQA
+// sharing), and every MFMA operand read from LDS feeds two MFMAs (one per row block).
+// With one wave per SIMD a wave may hold 512 registers: the two 32x256 fp32 output
+// accumulators live in AGPRs, the rotated Q fragments of both blocks in VGPRs.
 //
-// Per tile of 32 keys (double-buffered in LDS, one barrier per tile):
-//   * K rows are loaded, rotated (RoPE with the layer type's theta and width) in fp32,
-//     rounded to bf16 and stored row-major; V rows are stored transposed so both MFMA
-//     operands come from 16-byte LDS reads;
-//   * S^T = K * Q^T on v_mfma_f32_32x32x16_bf16 (Q, rotated once, stays in registers),
-//     so each lane owns one query row and its softmax statistics need no broadcast;
-//   * online softmax in fp32 / log2 domain; the running maximum is only moved when a new
-//     score exceeds it by more than 8 (so P <= 2^8), which makes the O rescale rare;
-//   * O^T += V^T * P^T on the same MFMA, accumulators in fp32.
-// Tiles wholly outside a wave's visible band are skipped; sliding layers only visit the
-// 512-key band (Spark-X2.6-4B-Base hybrid attention explainer, eliteato.com/news/34565,
-// section "滑动窗口 512": a token sees at most the last 512 tokens; full layers see every
-// earlier token, section "36 层混合注意力排布").
-// Epilogue: O / l * sigmoid(gate) (F16 vs Q4 comparison page, hotelren.com/news/5475707,
-// section 三: one sigmoid gate per head), stored as bf16.  The workgroup that owns a
-// key tile's positions also writes the rotated keys and values into the KV cache.
+// K/V tiles of 32 keys stream through a 3-stage LDS ring filled by direct global->LDS
+// loads (no register staging), issued two tiles ahead:
+//   * K tile, chunk-major (16-byte chunk c of key j at slot 32c + j): the MFMA A operand
+//     of S^T = K Q^T is one conflict-free 16-byte read.  RoPE is applied in place by the
+//     lane that loaded a rotary pair of chunks (m, m + r/2), right after its own load
+//     lands; on full layers only two waves hold rotary chunks.
+//   * V tile, row-major with the chunk index XOR-swizzled by 4 * (row % 4): the A operand
+//     of O^T += V^T P^T (V transposed) comes from two ds_read_b64_tr_b16 per MFMA, which
+//     transpose 16-bit elements across each group of 16 lanes.
+//   * S^T = K Q^T and O^T += V^T P^T on v_mfma_f32_32x32x16_bf16; each lane owns one
+//     query row per block, so softmax statistics need no broadcast.  Q is rotated and
+//     pre-scaled by log2(e)/16 once; the softmax runs in exp2 form in fp32; the running
+//     maximum moves only when a score exceeds it by more than 8 (P <= 2^8), so the O
+//     rescale is rare; row sums come from v_dot2_f32_bf16 on the rounded P.
+// Sliding layers visit only the 512-key band (Spark-X2.6-4B-Base hybrid attention
+// explainer, eliteato.com/news/34565, section "滑动窗口 512"); full layers every earlier
+// key (section "36 层混合注意力排布").  Epilogue: O / l * sigmoid(gate) (F16 vs Q4
+// comparison page, hotelren.com/news/5475707, section 三), stored as bf16.  The
+// workgroup owning a key tile's positions also writes its rotated keys and values into
+// the KV cache.
 #include "spark_device.hpp"
 #include "spark_launch.hpp"
+
+#include <type_traits>
 
 namespace spark {
 namespace {
 
-constexpr int kBM = 64;           // query positions per workgroup
-constexpr int kBN = 32;           // keys per tile
-constexpr int kThreads = 512;     // 8 waves
-constexpr int kKsStride = 264;    // bf16 per K row in LDS (256 + 8: conflict-free reads)
-constexpr int kVtStride = 40;     // bf16 per transposed V row (32 keys + 8)
-constexpr int kKsTile = kBN * kKsStride;
-constexpr int kVtTile = kHeadDim * kVtStride;
-constexpr float kRescaleThreshold = 8.0f;  // log2 units
+constexpr int kBM = 64;            // query positions per workgroup
+constexpr int kBN = 32;            // keys per tile
+constexpr int kWaves = 8;                          // waves per workgroup (4 or 8)
+constexpr int kRowBlocks = 8 / kWaves;            // 32-row blocks per wave
+constexpr int kThreads = 64 * kWaves;
+constexpr int kTileBytes = kBN * kHeadDim * 2;   // 16 KB per K or V tile
+constexpr float kRescaleThreshold = 8.0f;        // log2 units
+constexpr float kQScale = 0.0625f * 1.4426950408889634f;   // 1/sqrt(256) * log2(e)
 
-// Position of key `key` (0..31) of a tile inside a transposed V row: keys
-// 16t + 8a + 4h + b are stored at 16t + 8h + 4a + b, which is the order in which the
-// P^T operand of lane half h lists them (see the S^T result layout).
-__device__ __forceinline__ int vt_slot(int key) {
-  return (key & ~12) | ((key & 4) << 1) | ((key & 8) >> 1);
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+__device__ __forceinline__ void dma16(const void* src, void* lds_block) {
+  __builtin_amdgcn_global_load_lds(src, lds_block, 16, 0, 0);
 }
 
-struct KvStage {
-  u32x4 k[2];
-  u32x4 v[2];
-};
+// vmcnt <= N, other counters untouched.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Workgroup barrier that only waits for this wave's LDS operations.  __syncthreads()
+// would also wait for every outstanding global load, including the tile prefetched two
+// steps ahead; the loads a step depends on are waited for explicitly instead.
+__device__ __forceinline__ void barrier_lds() {
+  __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4));   // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+}
+
+// The K tile is filled by 16 load instructions; instruction n brings chunks 2n and 2n+1
+// of all 32 keys.  k_instr(w, q) is the q-th (of 4) that wave w issues, chosen so that a
+// rotary pair of chunks lands in one lane: instructions q = 0, 1 form one pair and
+// q = 2, 3 another.
+template <int LT>
+__device__ __forceinline__ int k_instr(int w, int q) {
+  if (kWaves == 4) {
+    if (LT == kSliding) return w + 4 * (q >> 1) + 8 * (q & 1);   // chunks c, c+16: dims d, d+128
+    if (w < 2) return q < 2 ? w + 2 * q : 4 + 2 * w + (q - 2);   // chunks c, c+4 (d < 32), then plain
+    return 8 + 4 * (w - 2) + q;                                  // chunks 16..31: plain
+  }
+  if (LT == kSliding) return w + 8 * q;                          // chunks c, c+16
+  if (w < 2) return w + 2 * q;                                   // chunks c, c+4 (d < 32)
+  return 2 * w + q;                                              // chunks 8..31: plain
+}
+
+constexpr int kKLoads = 16 / kWaves;              // K-tile load instructions per wave
+constexpr int kVLoads = 16 / kWaves;              // V-tile load instructions per wave
 
 template <int LT>
-__device__ __forceinline__ void k_chunk_offsets(int c, int& off_a, int& off_b, bool& rot) {
-  if (LT == kSliding) {          // pairs (d, d + 128): thread c owns d in [8c, 8c + 8)
-    off_a = 8 * c;
-    off_b = 128 + 8 * c;
-    rot = true;
-  } else if (c < 4) {            // pairs (d, d + 32) for d < 32
-    off_a = 8 * c;
-    off_b = 32 + 8 * c;
-    rot = true;
-  } else {                       // dims 64..255 are not rotated
-    off_a = 64 + 16 * (c - 4);
-    off_b = off_a + 8;
-    rot = false;
+__device__ __forceinline__ int k_rotary_pairs(int w) {         // rotary chunk pairs per lane
+  return LT == kSliding ? kKLoads / 2 : (w < 2 ? 1 : 0);
+}
+
+template <int LT>
+__device__ __forceinline__ void issue_tile(const PrefillArgs& a, int b, int g, int k0, int wave,
+                                           int lane, uint8_t* ks, uint8_t* vs) {
+  const int S = a.seq_len;
+  const size_t seq_row0 = (size_t)b * S;
+  const int pk = min(k0 + (lane & 31), S - 1);      // rows past the end: any valid row (masked)
+#pragma unroll
+  for (int q = 0; q < kKLoads; ++q) {
+    const int n = k_instr<LT>(wave, q);
+    const int chunk = 2 * n + (lane >> 5);
+    dma16(a.k + ((seq_row0 + pk) * kKvHeads + g) * kHeadDim + 8 * chunk, ks + n * 1024);
+  }
+#pragma unroll
+  for (int q = 0; q < kVLoads; ++q) {
+    const int n = kVLoads * wave + q;
+    const int r = 2 * n + (lane >> 5);
+    const int chunk = (lane & 31) ^ (4 * (r & 3));
+    const int p = min(k0 + r, S - 1);
+    dma16(a.v + ((seq_row0 + p) * kKvHeads + g) * kHeadDim + 8 * chunk, vs + n * 1024);
   }
 }
 
+// After this lane's loads of a tile have landed: rotate its rotary K chunk pairs in
+// place and, for the tiles of this workgroup's own positions, copy its K/V chunks to the
+// cache.
 template <int LT>
-__device__ __forceinline__ void load_tile(const PrefillArgs& a, int b, int g, int k0, int tid,
-                                          KvStage& st) {
+__device__ __forceinline__ void finish_tile(const PrefillArgs& a, int b, int g, int k0, int q0,
+                                            int wave, int lane, uint8_t* ks, uint8_t* vs,
+                                            const double* inv, bool& stored) {
   const int S = a.seq_len;
-  {  // K: thread -> (key = tid / 16, chunk pair c = tid % 16)
-    const int key = tid >> 4, c = tid & 15;
-    int off_a, off_b;
-    bool rot;
-    k_chunk_offsets<LT>(c, off_a, off_b, rot);
-    const int p = k0 + key;
-    if (p < S) {
-      const uint16_t* row = a.k + (((size_t)b * S + p) * kKvHeads + g) * kHeadDim;
-      st.k[0] = ld_global16(row + off_a);
-      st.k[1] = ld_global16(row + off_b);
-    } else {
-      st.k[0] = u32x4{0, 0, 0, 0};
-      st.k[1] = u32x4{0, 0, 0, 0};
+  const int key = lane & 31;
+  const int p = k0 + key;
+  const int npairs = k_rotary_pairs<LT>(wave);
+#pragma unroll
+  for (int pr = 0; pr < kKLoads / 2; ++pr) {
+    if (pr < npairs) {
+      const int na = k_instr<LT>(wave, 2 * pr), nb = k_instr<LT>(wave, 2 * pr + 1);
+      u32x4* pa = reinterpret_cast<u32x4*>(ks + na * 1024 + lane * 16);
+      u32x4* pb = reinterpret_cast<u32x4*>(ks + nb * 1024 + lane * 16);
+      u32x4 xa = *pa, xb = *pb;
+      rope_rotate_chunks(xa, xb, (double)p, inv, 8 * (2 * na + (lane >> 5)));
+      *pa = xa;
+      *pb = xb;
     }
   }
-  {  // V: thread -> (key = tid % 32, dims [8dc, 8dc+8) and [128+8dc, 128+8dc+8))
-    const int key = tid & 31, dc = tid >> 5;
-    const int p = k0 + key;
-    if (p < S) {
-      const uint16_t* row = a.v + (((size_t)b * S + p) * kKvHeads + g) * kHeadDim;
-      st.v[0] = ld_global16(row + 8 * dc);
-      st.v[1] = ld_global16(row + 128 + 8 * dc);
-    } else {
-      st.v[0] = u32x4{0, 0, 0, 0};
-      st.v[1] = u32x4{0, 0, 0, 0};
-    }
-  }
-}
-
-// Rotate the staged keys, write K and V^T into LDS, and (for tiles of this workgroup's
-// own positions) into the KV cache.
-template <int LT>
-__device__ __forceinline__ void store_tile(const PrefillArgs& a, int b, int g, int k0, int q0,
-                                           int tid, KvStage& st, uint16_t* ks, uint16_t* vt,
-                                           const double* inv) {
-  const int S = a.seq_len;
-  const int cap = a.cache_cap;
-  const bool own = a.cache_k != nullptr && k0 >= q0;
-  {
-    const int key = tid >> 4, c = tid & 15;
-    int off_a, off_b;
-    bool rot;
-    k_chunk_offsets<LT>(c, off_a, off_b, rot);
-    const int p = k0 + key;
-    if (rot) rope_rotate_chunks(st.k[0], st.k[1], (double)p, inv, off_a);
-    *reinterpret_cast<u32x4*>(ks + key * kKsStride + off_a) = st.k[0];
-    *reinterpret_cast<u32x4*>(ks + key * kKsStride + off_b) = st.k[1];
-    if (own && p < S && (LT == kFull || p >= S - kWindow)) {
+  if (a.cache_k != nullptr && k0 >= q0) {
+    stored = true;
+    const int cap = a.cache_cap;
+    if (p < S && (LT == kFull || p >= S - kWindow)) {
       const int slot = (LT == kFull) ? p : (p & (kWindow - 1));
       uint16_t* dst = a.cache_k + (((size_t)b * cap + slot) * kKvHeads + g) * kHeadDim;
-      st_global16(dst + off_a, st.k[0]);
-      st_global16(dst + off_b, st.k[1]);
-    }
-  }
-  {
-    const int key = tid & 31, dc = tid >> 5;
-    const int col = vt_slot(key);
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const int d0 = 128 * half + 8 * dc;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const uint32_t x = st.v[half][w];
-        vt[(d0 + 2 * w) * kVtStride + col] = (uint16_t)(x & 0xffffu);
-        vt[(d0 + 2 * w + 1) * kVtStride + col] = (uint16_t)(x >> 16);
+      for (int q = 0; q < kKLoads; ++q) {
+        const int n = k_instr<LT>(wave, q);
+        st_global16(dst + 8 * (2 * n + (lane >> 5)), *reinterpret_cast<const u32x4*>(ks + n * 1024 + lane * 16));
       }
     }
-    const int p = k0 + key;
-    if (own && p < S && (LT == kFull || p >= S - kWindow)) {
-      const int slot = (LT == kFull) ? p : (p & (kWindow - 1));
-      uint16_t* dst = a.cache_v + (((size_t)b * cap + slot) * kKvHeads + g) * kHeadDim;
-      st_global16(dst + 8 * dc, st.v[0]);
-      st_global16(dst + 128 + 8 * dc, st.v[1]);
+#pragma unroll
+    for (int q = 0; q < kVLoads; ++q) {
+      const int n = kVLoads * wave + q;
+      const int r = 2 * n + (lane >> 5);
+      const int pv = k0 + r;
+      if (pv < S && (LT == kFull || pv >= S - kWindow)) {
+        const int chunk = (lane & 31) ^ (4 * (r & 3));
+        const int slot = (LT == kFull) ? pv : (pv & (kWindow - 1));
+        uint16_t* dst = a.cache_v + (((size_t)b * cap + slot) * kKvHeads + g) * kHeadDim;
+        st_global16(dst + 8 * chunk, *reinterpret_cast<const u32x4*>(vs + n * 1024 + lane * 16));
+      }
+    }
+  }
+}
+
+// Workgroup -> (sequence, KV head, query block).  Workgroups are dealt round-robin to the
+// 8 XCDs; when the (sequence, KV head) units divide evenly over them, each XCD gets the
+// query blocks of one unit (so its L2 serves one K/V stream), alternating blocks between
+// the XCDs sharing a unit.  Full layers run the longest (latest) blocks first.
+template <int LT>
+__device__ __forceinline__ void block_coords(int id, int batch, int nqb, int& b, int& g, int& qb) {
+  const int units = batch * kKvHeads;
+  int unit, qidx;
+  if (8 % units == 0 && nqb % (8 / units) == 0) {
+    const int r = 8 / units;
+    const int x = id & 7, j = id >> 3;
+    unit = x / r;
+    qidx = r * j + (x % r);
+  } else {
+    unit = id % units;
+    qidx = id / units;
+  }
+  b = unit / kKvHeads;
+  g = unit % kKvHeads;
+  qb = (LT == kFull) ? (nqb - 1 - qidx) : qidx;
+}
+
+// Rotate (RoPE at position p) and scale the Q row slice this lane holds, into MFMA
+// B-operand fragments: fragment s holds dims 16s + 8*half + j.
+template <int LT>
+__device__ __forceinline__ void load_q(const PrefillArgs& a, int b, int hq, int row, int half,
+                                       const double* inv, bf16x8* qf) {
+  using T = LayerTraits<LT>;
+  const int S = a.seq_len;
+  u32x4 raw[16];
+  if (row < S) {
+    const uint16_t* qrow = a.q + (((size_t)b * S + row) * kQHeads + hq) * kHeadDim;
+#pragma unroll
+    for (int s = 0; s < 16; ++s) raw[s] = ld_global16(qrow + 16 * s + 8 * half);
+  } else {
+#pragma unroll
+    for (int s = 0; s < 16; ++s) raw[s] = u32x4{0, 0, 0, 0};
+  }
+  const double p = (double)row;
+  constexpr int kPairChunks = T::kRot / 32;         // fragment s pairs with s + kPairChunks
+#pragma unroll
+  for (int s = 0; s < 16; ++s) {
+    if (s < kPairChunks) {
+      u32x4 y1, y2;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        float c0, s0, c1, s1;
+        const int m = 16 * s + 8 * half + 2 * w;
+        rope_cos_sin(p, inv[m], c0, s0);
+        rope_cos_sin(p, inv[m + 1], c1, s1);
+        const float a0 = bf16_lo(raw[s][w]), a1 = bf16_hi(raw[s][w]);
+        const float b0 = bf16_lo(raw[s + kPairChunks][w]), b1 = bf16_hi(raw[s + kPairChunks][w]);
+        y1[w] = pack_bf16x2((a0 * c0 - b0 * s0) * kQScale, (a1 * c1 - b1 * s1) * kQScale);
+        y2[w] = pack_bf16x2((b0 * c0 + a0 * s0) * kQScale, (b1 * c1 + a1 * s1) * kQScale);
+      }
+      qf[s] = as_bf16x8(y1);
+      qf[s + kPairChunks] = as_bf16x8(y2);
+    } else if (s >= 2 * kPairChunks) {
+      u32x4 y;
+#pragma unroll
+      for (int w = 0; w < 4; ++w)
+        y[w] = pack_bf16x2(bf16_lo(raw[s][w]) * kQScale, bf16_hi(raw[s][w]) * kQScale);
+      qf[s] = as_bf16x8(y);
     }
   }
 }
 
 template <int LT>
-__global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves / 4, kWaves / 4)))
+void prefill_kernel(PrefillArgs a) {
   using T = LayerTraits<LT>;
-  __shared__ __attribute__((aligned(16))) uint16_t s_k[2 * kKsTile];
-  __shared__ __attribute__((aligned(16))) uint16_t s_vt[2 * kVtTile];
+  // One array per stage and operand: the loop below is unrolled by the stage count, so
+  // the compiler can tell that reads of one stage never alias the loads in flight into
+  // the others, and does not wait for those loads before reading.
+  __shared__ __attribute__((aligned(1024))) uint8_t s_k0[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t s_v0[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t s_k1[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t s_v1[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t s_k2[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t s_v2[kTileBytes];
   __shared__ double s_inv[T::kRot / 2];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // scalar: wave-uniform branches
   const int half = lane >> 5;
   const int r32 = lane & 31;
   const int S = a.seq_len;
-  const int units = a.batch * kKvHeads;
 
-  // Block order: full layers take the longest (latest) query blocks first.
-  const int id = blockIdx.x;
-  const int bg = id % units;
-  const int ord = id / units;
-  const int qb = (LT == kFull) ? (a.nqb - 1 - ord) : ord;
-  const int b = bg / kKvHeads;
-  const int g = bg % kKvHeads;
+  int b, g, qb;
+  block_coords<LT>(blockIdx.x, a.batch, a.nqb, b, g, qb);
   const int q0 = qb * kBM;
+  const int hq = g * kGroup + (kRowBlocks == 2 ? wave : wave >> 1);
+  const int rb0 = kRowBlocks == 2 ? 0 : (wave & 1);      // first 32-row block of this wave
 
-  if (tid < T::kRot / 2) s_inv[tid] = rope_inv_rev(tid, T::kRot, log2(T::kTheta));
-  __syncthreads();
-
-  // ---- Q fragments: lane holds row r32 of its 32-row slab, dims 16s + 8*half + j.
-  const int hq = g * kGroup + (wave >> 1);
-  const int r0 = q0 + 32 * (wave & 1);
-  const int row = r0 + r32;
-  bf16x8 qf[16];
-  {
-    u32x4 raw[16];
-    if (row < S) {
-      const uint16_t* qrow = a.q + (((size_t)b * S + row) * kQHeads + hq) * kHeadDim;
-#pragma unroll
-      for (int s = 0; s < 16; ++s) raw[s] = ld_global16(qrow + 16 * s + 8 * half);
-    } else {
-#pragma unroll
-      for (int s = 0; s < 16; ++s) raw[s] = u32x4{0, 0, 0, 0};
-    }
-    const double p = (double)row;
-    if (LT == kSliding) {        // chunk s pairs with chunk s + 8 (d + 128)
-#pragma unroll
-      for (int s = 0; s < 8; ++s) rope_rotate_chunks(raw[s], raw[s + 8], p, s_inv, 16 * s + 8 * half);
-    } else {                     // chunk s (s < 2) pairs with chunk s + 2 (d + 32)
-#pragma unroll
-      for (int s = 0; s < 2; ++s) rope_rotate_chunks(raw[s], raw[s + 2], p, s_inv, 16 * s + 8 * half);
-    }
-#pragma unroll
-    for (int s = 0; s < 16; ++s) qf[s] = as_bf16x8(raw[s]);
-  }
-
-  // ---- key tiles this workgroup visits
   const int hi_key = min(q0 + kBM - 1, S - 1);
   const int lo_key = T::kWindowed ? max(0, q0 - (kWindow - 1)) : 0;
   const int kt_lo = lo_key / kBN;
   const int kt_hi = hi_key / kBN;
 
-  f32x16 o[8];
+  // Start streaming the first two tiles before anything else.
+  issue_tile<LT>(a, b, g, kt_lo * kBN, wave, lane, s_k0, s_v0);
+  if (kt_lo + 1 <= kt_hi) issue_tile<LT>(a, b, g, (kt_lo + 1) * kBN, wave, lane, s_k1, s_v1);
+
+  if (tid < T::kRot / 2) s_inv[tid] = rope_inv_rev(tid, T::kRot, log2(T::kTheta));
+  barrier_lds();
+
+  // Q fragments of both 32-row blocks: lane holds row r32 of each.
+  bf16x8 qf[kRowBlocks][16];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) o[i] = f32x16{0};
-  float m_run = -1e30f;
-  float l_part = 0.0f;
+  for (int rb = 0; rb < kRowBlocks; ++rb) load_q<LT>(a, b, hq, q0 + 32 * (rb0 + rb) + r32, half, s_inv, qf[rb]);
 
-  KvStage st;
-  load_tile<LT>(a, b, g, kt_lo * kBN, tid, st);
-  store_tile<LT>(a, b, g, kt_lo * kBN, q0, tid, st, s_k, s_vt, s_inv);
-  __syncthreads();
+  // First tile: wait for this lane's loads, rotate, publish.  Waiting for the second
+  // tile too leaves no load in flight on entry to the loop, which lets the compiler keep
+  // exact track of the loads in flight per stage inside it.
+  bool stored = false;
+  wait_vmcnt<0>();
+  finish_tile<LT>(a, b, g, kt_lo * kBN, q0, wave, lane, s_k0, s_v0, s_inv, stored);
+  barrier_lds();
 
-  for (int kt = kt_lo; kt <= kt_hi; ++kt) {
-    const int buf = (kt - kt_lo) & 1;
+  f32x16 o[kRowBlocks][8];
+  float m_run[kRowBlocks], l_part[kRowBlocks];
+#pragma unroll
+  for (int rb = 0; rb < kRowBlocks; ++rb) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o[rb][i] = f32x16{0};
+    m_run[rb] = -1e30f;
+    l_part[rb] = 0.0f;
+  }
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+
+  // Per-lane byte offsets of the transposed V reads: lane l = 16 grp + 4 vr + vc provides
+  // row 4*(grp/2) + vr (+8 for the second read of a fragment) and dims
+  // 32 db + 16 (grp & 1) + 4 vc of the tile; chunk positions are swizzled by 4 * vr.
+  const int grp = lane >> 4, vr = (lane >> 2) & 3, vc = lane & 3;
+  const int v_lane_off = (4 * (grp >> 1) + vr) * 512 + 16 * (2 * (grp & 1) + (vc >> 1)) + 8 * (vc & 1);
+
+  // One pipeline step on tile kt held in stage ST: start loading tile kt+2 into stage
+  // ST+2, compute tile kt, then finish tile kt+1 (stage ST+1) and publish it.
+  auto step = [&](auto stage_tag, int kt) {
+    constexpr int ST = decltype(stage_tag)::value;
+    uint8_t* const ks = ST == 0 ? s_k0 : ST == 1 ? s_k1 : s_k2;
+    uint8_t* const vs = ST == 0 ? s_v0 : ST == 1 ? s_v1 : s_v2;
+    uint8_t* const ks1 = ST == 0 ? s_k1 : ST == 1 ? s_k2 : s_k0;
+    uint8_t* const vs1 = ST == 0 ? s_v1 : ST == 1 ? s_v2 : s_v0;
+    uint8_t* const ks2 = ST == 0 ? s_k2 : ST == 1 ? s_k0 : s_k1;
+    uint8_t* const vs2 = ST == 0 ? s_v2 : ST == 1 ? s_v0 : s_v1;
     const int k0 = kt * kBN;
-    const bool more = kt < kt_hi;
-    if (more) load_tile<LT>(a, b, g, k0 + kBN, tid, st);
+    const bool two_ahead = kt + 2 <= kt_hi;
+    // The compiler cannot follow per-stage loads across the loop back edge, so the first
+    // LDS read of step 0 waits for every load in flight; step 0 therefore starts its
+    // prefetch after its MFMAs, the other steps before theirs.
+    if (ST != 0 && two_ahead) issue_tile<LT>(a, b, g, k0 + 2 * kBN, wave, lane, ks2, vs2);
 
-    const uint16_t* ks = s_k + buf * kKsTile;
-    const uint16_t* vt = s_vt + buf * kVtTile;
-    // Wave-uniform visibility of this tile for rows r0..r0+31.
-    const bool any = (k0 <= r0 + 31) && (!T::kWindowed || k0 + kBN - 1 >= r0 - (kWindow - 1));
-    if (any) {
-      f32x16 sacc = f32x16{0};
+    // Which row blocks see any key of this tile (wave-uniform).
+    bool any[kRowBlocks], edge[kRowBlocks], any_rb = false;
+#pragma unroll
+    for (int rb = 0; rb < kRowBlocks; ++rb) {
+      const int r0 = q0 + 32 * (rb0 + rb);
+      any[rb] = (k0 <= r0 + 31) && (!T::kWindowed || k0 + kBN - 1 >= r0 - (kWindow - 1));
+      edge[rb] = (k0 + kBN - 1 > r0) || (T::kWindowed && k0 < r0 + 31 - (kWindow - 1));
+      any_rb = any_rb || any[rb];
+    }
+    if (any_rb) {
+      f32x16 sacc[kRowBlocks];
+#pragma unroll
+      for (int rb = 0; rb < kRowBlocks; ++rb) sacc[rb] = f32x16{0};
 #pragma unroll
       for (int s = 0; s < 16; ++s) {
-        const bf16x8 ka = as_bf16x8(*reinterpret_cast<const u32x4*>(ks + r32 * kKsStride + 16 * s + 8 * half));
-        sacc = mfma_32x32x16(ka, qf[s], sacc);
+        const bf16x8 ka = as_bf16x8(*reinterpret_cast<const u32x4*>(ks + (32 * (2 * s + half) + r32) * 16));
+#pragma unroll
+        for (int rb = 0; rb < kRowBlocks; ++rb) sacc[rb] = mfma_32x32x16(ka, qf[rb][s], sacc[rb]);
       }
-      float t[16];
+      bf16x8 pf[kRowBlocks][2];
 #pragma unroll
-      for (int v = 0; v < 16; ++v) t[v] = sacc[v] * kScoreScaleLog2;
-      const bool edge = (k0 + kBN - 1 > r0) || (T::kWindowed && k0 < r0 + 31 - (kWindow - 1));
-      if (edge) {
+      for (int rb = 0; rb < kRowBlocks; ++rb) {
+        const int row = q0 + 32 * (rb0 + rb) + r32;
+        if (edge[rb]) {
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int key = k0 + 8 * (v >> 2) + 4 * half + (v & 3);
-          const bool vis = key <= row && (!T::kWindowed || key > row - kWindow);
-          t[v] = vis ? t[v] : -INFINITY;
+          for (int v = 0; v < 16; ++v) {
+            const int key = k0 + 8 * (v >> 2) + 4 * half + (v & 3);
+            const bool vis = key <= row && (!T::kWindowed || key > row - kWindow);
+            sacc[rb][v] = vis ? sacc[rb][v] : -INFINITY;
+          }
         }
-      }
-      float mt = t[0];
+        float mt = fmaxf(sacc[rb][0], sacc[rb][1]);
 #pragma unroll
-      for (int v = 1; v < 16; ++v) mt = fmaxf(mt, t[v]);
-      mt = fmaxf(mt, __shfl_xor(mt, 32));
-      if (__any(mt > m_run + kRescaleThreshold)) {
-        const float m_new = fmaxf(m_run, mt);
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-        l_part *= alpha;
+        for (int v = 2; v < 16; ++v) mt = fmaxf(mt, sacc[rb][v]);
+        mt = fmaxf(mt, __shfl_xor(mt, 32));
+        if (__any(mt > m_run[rb] + kRescaleThreshold)) {
+          const float m_new = fmaxf(m_run[rb], mt);
+          const float alpha = __builtin_amdgcn_exp2f(m_run[rb] - m_new);
+          l_part[rb] *= alpha;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) o[i] *= alpha;
-        m_run = m_new;
-      }
-      bf16x8 pf[2];
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
-        u32x4 pk;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const float p0 = __builtin_amdgcn_exp2f(t[8 * tt + 2 * w] - m_run);
-          const float p1 = __builtin_amdgcn_exp2f(t[8 * tt + 2 * w + 1] - m_run);
-          pk[w] = pack_bf16x2(p0, p1);
-          l_part += bf16_lo(pk[w]) + bf16_hi(pk[w]);
+          for (int i = 0; i < 8; ++i) o[rb][i] *= alpha;
+          m_run[rb] = m_new;
         }
-        pf[tt] = as_bf16x8(pk);
-      }
-#pragma unroll
-      for (int db = 0; db < 8; ++db) {
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
-          const bf16x8 va = as_bf16x8(*reinterpret_cast<const u32x4*>(
-              vt + (32 * db + r32) * kVtStride + 16 * tt + 8 * half));
-          o[db] = mfma_32x32x16(va, pf[tt], o[db]);
+          u32x4 pk;
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            // The pair is built as bf16x2 and then stored into pk, not read back out of
+            // pk: hipcc (ROCm 7.2) folds a bf16x2 bit-cast of pk[w] to pk[0] for every w.
+            const bf16x2 p2 = {(__bf16)__builtin_amdgcn_exp2f(sacc[rb][8 * tt + 2 * w] - m_run[rb]),
+                               (__bf16)__builtin_amdgcn_exp2f(sacc[rb][8 * tt + 2 * w + 1] - m_run[rb])};
+            l_part[rb] = __builtin_amdgcn_fdot2_f32_bf16(p2, ones, l_part[rb], false);
+            pk[w] = __builtin_bit_cast(uint32_t, p2);
+          }
+          pf[rb][tt] = as_bf16x8(pk);
+        }
+      }
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+#pragma unroll
+        for (int db = 0; db < 8; ++db) {
+          const int off = v_lane_off + 16 * tt * 512 + 64 * (db ^ vr);
+          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vs + off));
+          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vs + off + 8 * 512));
+          const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+          for (int rb = 0; rb < kRowBlocks; ++rb) o[rb][db] = mfma_32x32x16(va, pf[rb][tt], o[rb][db]);
         }
       }
     }
+    if (ST == 0 && two_ahead) issue_tile<LT>(a, b, g, k0 + 2 * kBN, wave, lane, ks2, vs2);
+    if (kt + 1 <= kt_hi) {
+      // This lane's loads of tile kt+1 were issued one step ago; tile kt+2's may still be
+      // in flight.  Cache stores also count, so after any, wait for all.  Every lane waits
+      // for its own loads before the barrier: other waves read them.
+      if (two_ahead && !stored) wait_vmcnt<kKLoads + kVLoads>(); else wait_vmcnt<0>();
+      finish_tile<LT>(a, b, g, k0 + kBN, q0, wave, lane, ks1, vs1, s_inv, stored);
+    }
+    barrier_lds();
+    __builtin_amdgcn_sched_barrier(0);   // keep the unrolled steps apart (register pressure)
+  };
 
-    if (more) store_tile<LT>(a, b, g, k0 + kBN, q0, tid, st, s_k + (buf ^ 1) * kKsTile,
-                             s_vt + (buf ^ 1) * kVtTile, s_inv);
-    __syncthreads();
+  for (int kt = kt_lo;;) {
+    step(std::integral_constant<int, 0>{}, kt);
+    if (++kt > kt_hi) break;
+    step(std::integral_constant<int, 1>{}, kt);
+    if (++kt > kt_hi) break;
+    step(std::integral_constant<int, 2>{}, kt);
+    if (++kt > kt_hi) break;
   }
 
   // ---- epilogue: O / l * sigmoid(gate), bf16
-  const float l_tot = l_part + __shfl_xor(l_part, 32);
-  if (row < S) {
-    const float gl = bf16_to_f32(a.gate[((size_t)b * S + row) * kQHeads + hq]);
-    const float scale = sigmoidf_fast(gl) / l_tot;
-    uint16_t* orow = a.out + (((size_t)b * S + row) * kQHeads + hq) * kHeadDim;
 #pragma unroll
-    for (int db = 0; db < 8; ++db) {
+  for (int rb = 0; rb < kRowBlocks; ++rb) {
+    const int row = q0 + 32 * (rb0 + rb) + r32;
+    const float l_tot = l_part[rb] + __shfl_xor(l_part[rb], 32);
+    if (row < S) {
+      const float gl = bf16_to_f32(a.gate[((size_t)b * S + row) * kQHeads + hq]);
+      const float scale = sigmoidf_fast(gl) / l_tot;
+      uint16_t* orow = a.out + (((size_t)b * S + row) * kQHeads + hq) * kHeadDim;
 #pragma unroll
-      for (int qd = 0; qd < 4; ++qd) {
-        u32x2 w;
-        w[0] = pack_bf16x2(o[db][4 * qd] * scale, o[db][4 * qd + 1] * scale);
-        w[1] = pack_bf16x2(o[db][4 * qd + 2] * scale, o[db][4 * qd + 3] * scale);
-        *reinterpret_cast<u32x2*>(orow + 32 * db + 8 * qd + 4 * half) = w;
+      for (int db = 0; db < 8; ++db) {
+#pragma unroll
+        for (int qd = 0; qd < 4; ++qd) {
+          u32x2 w;
+          w[0] = pack_bf16x2(o[rb][db][4 * qd] * scale, o[rb][db][4 * qd + 1] * scale);
+          w[1] = pack_bf16x2(o[rb][db][4 * qd + 2] * scale, o[rb][db][4 * qd + 3] * scale);
+          *reinterpret_cast<u32x2*>(orow + 32 * db + 8 * qd + 4 * half) = w;
+        }
       }
     }
   }

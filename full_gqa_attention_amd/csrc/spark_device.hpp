@@ -108,6 +108,9 @@ __device__ __forceinline__ void rope_rotate_chunks(u32x4& x1, u32x4& x2, double 
     const float b0 = bf16_lo(x2[w]), b1 = bf16_hi(x2[w]);
     y1[w] = pack_bf16x2(a0 * c0 - b0 * s0, a1 * c1 - b1 * s1);
     y2[w] = pack_bf16x2(b0 * c0 + a0 * s0, b1 * c1 + a1 * s1);
+    // One pair of rotations at a time: overlapping all eight sin/cos evaluations (with
+    // their fp64 angle reductions) costs registers the callers cannot spare.
+    __builtin_amdgcn_sched_barrier(0);
   }
   x1 = y1;
   x2 = y2;
