@@ -95,6 +95,39 @@ def bench_decode(fga, synth, steps, warmup):
     return {"ms": ms, "bytes": kv_bytes + io_bytes, "gbs": gbs, "lens_sum": int(lens.sum())}
 
 
+def copy_calibration():
+    """Device-to-device copy of 4 GiB: the plain copy of known size that scales the HBM
+    traffic counters (run under rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE)."""
+    import torch
+    n = 1 << 31                                   # bf16 elements: 4 GiB
+    x = torch.ones(n, dtype=torch.bfloat16, device="cuda")
+    y = torch.empty_like(x)
+    ms = time_launches(lambda: y.copy_(x), 3, 1)
+    print(json.dumps({"copy_bytes_read": 2 * n, "copy_bytes_written": 2 * n, "ms": ms,
+                      "read_plus_write_gbs": 4 * n / (ms * 1e-3) / 1e9}), flush=True)
+
+
+def kernel_source_hash(files):
+    import hashlib
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, "full_gqa_attention_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch of ``kernel`` recorded in profiles/traffic.json, or None when the
+    kernel's sources changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path)).get(kernel)
+    if not rec or rec.get("source_hash") != kernel_source_hash(rec["sources"]):
+        return None
+    return rec["hbm_bytes_per_launch"]
+
+
 def cpu_baseline(synth, budget_s=12.0, S=8192):
     """The oracle, as it stands, on randomly sampled query rows of the prefill workload."""
     import numpy as np
@@ -131,6 +164,8 @@ def main():
     ap.add_argument("--skip-decode", action="store_true")
     ap.add_argument("--skip-prefill", action="store_true")
     ap.add_argument("--skip-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run the 4 GiB device copy used to scale traffic counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the path has no "
@@ -142,6 +177,9 @@ def main():
     import synth
 
     assert torch.cuda.is_available(), "bench.py needs the GPU"
+    if args.copy_calibration:
+        copy_calibration()
+        return
     result = {
         "metric": METRIC, "value": None, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": None, "higher_is_better": True, "scaling": "weak",
@@ -158,7 +196,7 @@ def main():
         result["ms_per_step"] = p["ms"]
         result["roofline"] = {"bound": "mfma", "achieved": p["tflops"], "peak": PEAK_BF16_TFLOPS,
                               "unit": "TFLOP/s", "frac": p["tflops"] / PEAK_BF16_TFLOPS,
-                              "traffic": None}
+                              "traffic": measured_traffic("prefill_full")}
         log(f"prefill {p['ms']:.3f} ms  {p['tflops']:.1f} TFLOP/s")
     if not args.skip_decode:
         log("decode ...")
@@ -168,7 +206,7 @@ def main():
                         "layer, bf16 KV [ctx, 4, 256]",
             "value": d["gbs"], "unit": "GB/s", "ms_per_step": d["ms"],
             "roofline": {"bound": "hbm", "achieved": d["gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                         "frac": d["gbs"] / PEAK_HBM_GBS, "traffic": None},
+                         "frac": d["gbs"] / PEAK_HBM_GBS, "traffic": measured_traffic("decode_full")},
         }
         log(f"decode {d['ms']:.3f} ms  {d['gbs']:.0f} GB/s")
     if not args.skip_cpu_baseline:
