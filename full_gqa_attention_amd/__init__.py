@@ -172,14 +172,15 @@ def kv_append(layer_type: int, k, v, pos, cache: KVCache, stream=None):
         raise SparkError(st, "spark_kv_append")
 
 
-def decode_workspace_bytes(layer_type: int, batch: int, max_seq_len: int, split_keys: int = 0) -> int:
+def decode_workspace_bytes(layer_type: int, batch: int, max_seq_len: int, num_parts: int = 0) -> int:
     return int(_lib.spark_attn_decode_workspace_bytes(int(layer_type), int(batch), int(max_seq_len),
-                                                      int(split_keys)))
+                                                      int(num_parts)))
 
 
 def decode(layer_type: int, q, gate, cache: KVCache, seq_lens, max_seq_len: int, out=None,
-           workspace=None, split_keys: int = 0, stream=None):
-    """spark_attn_decode: q [B,16,256] (pre-RoPE), gate [B,16], seq_lens device int32 [B]."""
+           workspace=None, num_parts: int = 0, stream=None):
+    """spark_attn_decode: q [B,16,256] (pre-RoPE), gate [B,16], seq_lens device int32 [B];
+    ``num_parts`` workgroups share the batch's keys (0: the library's choice)."""
     torch = _torch()
     B = int(q.shape[0])
     _check(q, "q", (B, N_Q_HEADS, HEAD_DIM), torch.bfloat16)
@@ -187,7 +188,7 @@ def decode(layer_type: int, q, gate, cache: KVCache, seq_lens, max_seq_len: int,
     _check(seq_lens, "seq_lens", (B,), torch.int32)
     if cache.layer_type != layer_type:
         raise ValueError("cache layer type differs from the call's")
-    need = decode_workspace_bytes(layer_type, B, max_seq_len, split_keys)
+    need = decode_workspace_bytes(layer_type, B, max_seq_len, num_parts)
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
     _check(workspace, "workspace", None, torch.uint8)
@@ -195,7 +196,7 @@ def decode(layer_type: int, q, gate, cache: KVCache, seq_lens, max_seq_len: int,
         out = torch.empty_like(q)
     _check(out, "out", tuple(q.shape), torch.bfloat16)
     st = _lib.spark_attn_decode(int(layer_type), B, _ptr(q), _ptr(gate), ctypes.pointer(cache.desc()),
-                                _ptr(seq_lens), int(max_seq_len), int(split_keys), _ptr(workspace),
+                                _ptr(seq_lens), int(max_seq_len), int(num_parts), _ptr(workspace),
                                 int(workspace.numel()), _ptr(out), _stream(stream))
     if st:
         raise SparkError(st, "spark_attn_decode")

@@ -9,6 +9,7 @@ namespace {
 
 constexpr int32_t kMaxBatch = 65535;
 constexpr int32_t kMaxSeq = 1 << 20;   // native context of the model: 1,048,576 positions
+constexpr int32_t kMaxParts = 1 << 20; // decode partitions (workgroups of the attention launch)
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned2(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 1u) == 0; }
@@ -99,21 +100,21 @@ spark_status spark_kv_append(int32_t layer_type, int32_t batch, int32_t n_new,
 }
 
 size_t spark_attn_decode_workspace_bytes(int32_t layer_type, int32_t batch, int32_t max_seq_len,
-                                         int32_t split_keys) {
+                                         int32_t num_parts) {
   if (!valid_type(layer_type) || batch < 1 || batch > kMaxBatch || max_seq_len < 1 ||
-      max_seq_len > kMaxSeq || split_keys < 0 || (split_keys % 32) != 0)
+      max_seq_len > kMaxSeq || num_parts < 0 || num_parts > kMaxParts)
     return 0;
-  return spark::plan_decode(layer_type, batch, max_seq_len, split_keys).total_bytes;
+  return spark::plan_decode(layer_type, batch, max_seq_len, num_parts).total_bytes;
 }
 
 spark_status spark_attn_decode(int32_t layer_type, int32_t batch, const void* q,
                                const void* gate_logits, const spark_kv_cache* cache,
                                const int32_t* seq_lens, int32_t max_seq_len,
-                               int32_t split_keys, void* workspace,
+                               int32_t num_parts, void* workspace,
                                size_t workspace_bytes, void* out, void* stream) {
   if (!valid_type(layer_type)) return SPARK_ERR_INVALID_ARG;
   if (batch < 1 || batch > kMaxBatch || max_seq_len < 1 || max_seq_len > kMaxSeq) return SPARK_ERR_INVALID_ARG;
-  if (split_keys < 0 || (split_keys % 32) != 0) return SPARK_ERR_INVALID_ARG;
+  if (num_parts < 0 || num_parts > kMaxParts) return SPARK_ERR_INVALID_ARG;
   if (!q || !gate_logits || !seq_lens || !out || !workspace) return SPARK_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(out) || !aligned2(gate_logits) ||
       (reinterpret_cast<uintptr_t>(seq_lens) & 3u) || (reinterpret_cast<uintptr_t>(workspace) & 255u))
@@ -121,23 +122,25 @@ spark_status spark_attn_decode(int32_t layer_type, int32_t batch, const void* q,
   const spark_status cs = check_cache(layer_type, cache, batch);
   if (cs != SPARK_OK) return cs;
   if (layer_type == SPARK_LAYER_FULL && max_seq_len > cache->capacity) return SPARK_ERR_INVALID_ARG;
-  const spark::DecodePlan plan = spark::plan_decode(layer_type, batch, max_seq_len, split_keys);
+  // Planned on max_seq_len (not the capacity), exactly as the workspace query plans it.
+  const spark::DecodePlan plan = spark::plan_decode(layer_type, batch, max_seq_len, num_parts);
   if (workspace_bytes < plan.total_bytes) return SPARK_ERR_WORKSPACE;
 
+  char* ws = static_cast<char*>(workspace);
   spark::DecodeArgs a{};
   a.q = static_cast<const uint16_t*>(q);
   a.gate = static_cast<const uint16_t*>(gate_logits);
   a.cache_k = static_cast<const uint16_t*>(cache->k);
   a.cache_v = static_cast<const uint16_t*>(cache->v);
   a.seq_lens = seq_lens;
-  a.ws_o = static_cast<float*>(workspace);
-  a.ws_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                     ((plan.ws_o_bytes + 255) & ~static_cast<size_t>(255)));
+  a.ws_cum = reinterpret_cast<int32_t*>(ws + plan.cum_offset);
+  a.ws_first = reinterpret_cast<int32_t*>(ws + plan.first_offset);
+  a.ws_o = reinterpret_cast<float*>(ws + plan.o_offset);
+  a.ws_ml = reinterpret_cast<float*>(ws + plan.ml_offset);
   a.out = static_cast<uint16_t*>(out);
   a.batch = batch;
   a.cache_cap = cache->capacity;
-  a.nsplit = plan.nsplit;
-  a.split_keys = plan.split_keys;
+  a.nparts = plan.nparts;
   return from_hip(spark::launch_decode(layer_type, a, static_cast<hipStream_t>(stream)));
 }
 

@@ -2,17 +2,26 @@
 //
 // Decode is bound by streaming the KV cache from HBM (F16 vs Q4 comparison page,
 // hotelren.com/news/5475707, section 二: each generated token re-reads its state), so
-// every cache byte is read exactly once: a workgroup (sequence b, split s) has one wave
-// per KV head, and that wave scores the 4 query heads sharing the head against each key
-// row it loads (GQA, Spark-X2.6-4B-Base explainer, eliteato.com/news/34565, section
-// "配套效率设计").  Per chunk of 32 keys:
-//   * S = Q K^T on v_mfma_f32_16x16x32_bf16 (rows = the 4 query heads, padded to 16),
-//     K rows loaded straight into the B operand (64 contiguous bytes per key per load);
-//   * online softmax in fp32 / log2 domain across the 16 lanes that hold the scores;
-//   * O += P V on the VALU in fp32: V rows are loaded fully coalesced (two 512-byte rows
-//     per instruction), each lane owns 8 dims of one key parity, P comes from LDS.
-// Each split writes (max, sum, unnormalised O) per query head to the workspace; a second
-// kernel merges the splits with log-sum-exp weights and applies the sigmoid head gate.
+// every cache byte is read exactly once and the whole batch's reads are spread evenly
+// over the workgroups:
+//   * plan: sequence b owns c_b = ceil(n_b / 32) chunks of 32 visible keys; the chunks of
+//     all sequences are numbered back to back (prefix sums cum[b]) and partition w of P
+//     takes chunks [floor(wC/P), floor((w+1)C/P)).  A one-workgroup kernel computes cum
+//     and the first sequence of each partition on the device, so no host sync is needed
+//     and uneven context lengths still give every workgroup the same amount of traffic.
+//   * split: workgroup w walks its chunks; each run of chunks inside one sequence is a
+//     segment with its own online softmax, written as a partial result (max, sum,
+//     unnormalised O per query head) to slot w + b, which is unique because both w and b
+//     only grow along the partition.  The workgroup has one wave per KV head, and that
+//     wave scores the 4 query heads sharing the head against each key row it loads (GQA,
+//     Spark-X2.6-4B-Base explainer, eliteato.com/news/34565, section "配套效率设计"):
+//       - S = Q K^T on v_mfma_f32_16x16x32_bf16 (rows = the 4 query heads, padded to 16),
+//         K rows loaded straight into the B operand (64 contiguous bytes per key per load);
+//       - online softmax in fp32 / log2 domain across the 16 lanes that hold the scores;
+//       - O += P V on the VALU in fp32: V rows are loaded fully coalesced (two 512-byte
+//         rows per instruction), each lane owns 8 dims of one key parity, P from LDS.
+//   * merge: per (sequence, query head), the partials of the partitions that touched the
+//     sequence are combined with log-sum-exp weights and the sigmoid head gate is applied.
 // Sliding layers read the 512-slot ring; full layers the contiguous cache.
 #include "spark_device.hpp"
 #include "spark_launch.hpp"
@@ -21,35 +30,70 @@ namespace spark {
 namespace {
 
 constexpr int kThreads = 256;   // 4 waves = 4 KV heads
-constexpr int kChunk = 32;      // keys per inner iteration
+constexpr int kChunk = 32;      // keys per inner iteration and per partition unit
 constexpr int kSlot = kKvHeads * kHeadDim;   // bf16 per cache slot
+constexpr int kPlanThreads = 1024;
 
 template <int LT>
-__device__ __forceinline__ int visible_keys(int L) {
-  return LT == kFull ? L : min(L, kWindow);
+__device__ __forceinline__ int visible_keys(int L, int cap) {
+  const int n = LT == kFull ? L : min(L, kWindow);
+  return max(0, min(n, cap));   // never read past the cache; L < 1 sees nothing
 }
 
 template <int LT>
-__global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
-  using T = LayerTraits<LT>;
-  __shared__ double s_inv[T::kRot / 2];
-  __shared__ __attribute__((aligned(16))) float s_p[kKvHeads][kChunk][4];
-  __shared__ __attribute__((aligned(16))) float s_alpha[kKvHeads][4];
+__device__ __forceinline__ int chunks_of(int L, int cap) {
+  return (visible_keys<LT>(L, cap) + kChunk - 1) / kChunk;
+}
 
-  const int split = blockIdx.x;
-  const int b = blockIdx.y;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int g = tid >> 6;
-  const int L = a.seq_lens[b];
-  const int n = min(visible_keys<LT>(L), a.cache_cap);   // never read past the cache
-  const int ks = split * a.split_keys;
-  if (ks >= n) return;                      // uniform over the workgroup
-  const int ke = min(ks + a.split_keys, n);
+// First chunk of partition w: floor(w C / P).
+__device__ __forceinline__ int part_lo(int w, int C, int P) {
+  return (int)(((long long)w * C) / P);
+}
 
-  if (tid < T::kRot / 2) s_inv[tid] = rope_inv_rev(tid, T::kRot, log2(T::kTheta));
+// Partition holding chunk x: the largest w with floor(w C / P) <= x.
+__device__ __forceinline__ int part_of(int x, int C, int P) {
+  return (int)((((long long)(x + 1) * P) + C - 1) / C) - 1;
+}
+
+template <int LT>
+__global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(DecodeArgs a) {
+  __shared__ int s_scan[kPlanThreads];
+  const int t = threadIdx.x;
+  const int per = (a.batch + kPlanThreads - 1) / kPlanThreads;
+  const int b0 = min(t * per, a.batch);
+  const int b1 = min(b0 + per, a.batch);
+  int own = 0;
+  for (int b = b0; b < b1; ++b) own += chunks_of<LT>(a.seq_lens[b], a.cache_cap);
+  s_scan[t] = own;
   __syncthreads();
+  for (int off = 1; off < kPlanThreads; off <<= 1) {
+    const int add = t >= off ? s_scan[t - off] : 0;
+    __syncthreads();
+    s_scan[t] += add;
+    __syncthreads();
+  }
+  const int C = s_scan[kPlanThreads - 1];
+  int run = s_scan[t] - own;
+  for (int b = b0; b < b1; ++b) {
+    const int c = chunks_of<LT>(a.seq_lens[b], a.cache_cap);
+    a.ws_cum[b] = run;
+    if (c > 0) {
+      // Partitions whose first chunk falls in [run, run + c) start in sequence b.
+      const int w0 = (int)(((long long)run * a.nparts + C - 1) / C);
+      const int w1 = (int)(((long long)(run + c) * a.nparts + C - 1) / C);
+      for (int w = w0; w < w1; ++w) a.ws_first[w] = b;
+    }
+    run += c;
+  }
+  if (t == kPlanThreads - 1) a.ws_cum[a.batch] = C;
+}
 
+// Online-softmax attention of the 4 query heads of KV head g of sequence b over keys
+// [ks, ke) of its cache; writes the partial result to slot `slot`.
+template <int LT>
+__device__ __forceinline__ void attend_segment(const DecodeArgs& a, int b, int L, int ks, int ke,
+                                               int slot, int g, int lane, const double* s_inv,
+                                               float (*s_p)[kChunk][4], float (*s_alpha)[4]) {
   // Q as the A operand: lane l holds head l % 16 (only 0..3 are real), dims 32s + 8(l/16) + j.
   const int hrow = lane & 15;
   const int kq = lane >> 4;
@@ -171,13 +215,13 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
     __builtin_amdgcn_wave_barrier();
   }
 
-  // Merge the two key parities, then write this split's partial results.
+  // Merge the two key parities, then write this segment's partial results.
 #pragma unroll
   for (int h = 0; h < 4; ++h)
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[h][e] += __shfl_xor(acc[h][e], 32);
 
-  const size_t head0 = ((size_t)b * a.nsplit + split) * kQHeads + g * kGroup;
+  const size_t head0 = (size_t)slot * kQHeads + g * kGroup;
   if (lane < 32) {
 #pragma unroll
     for (int h = 0; h < 4; ++h) {
@@ -196,55 +240,121 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
 }
 
 template <int LT>
+__global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
+  using T = LayerTraits<LT>;
+  __shared__ double s_inv[T::kRot / 2];
+  __shared__ __attribute__((aligned(16))) float s_p[kKvHeads][kChunk][4];
+  __shared__ __attribute__((aligned(16))) float s_alpha[kKvHeads][4];
+
+  const int w = blockIdx.x;
+  const int C = a.ws_cum[a.batch];
+  const int lo = part_lo(w, C, a.nparts);
+  const int hi = part_lo(w + 1, C, a.nparts);
+  if (lo >= hi) return;                      // uniform over the workgroup
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int g = __builtin_amdgcn_readfirstlane(tid >> 6);
+  if (tid < T::kRot / 2) s_inv[tid] = rope_inv_rev(tid, T::kRot, log2(T::kTheta));
+  __syncthreads();
+
+  int b = a.ws_first[w];
+  int cb = a.ws_cum[b];
+  for (;;) {
+    const int cn = a.ws_cum[b + 1];
+    if (cn > cb) {
+      const int L = a.seq_lens[b];
+      const int n = visible_keys<LT>(L, a.cache_cap);
+      const int ks = (max(lo, cb) - cb) * kChunk;
+      const int ke = min((min(hi, cn) - cb) * kChunk, n);
+      attend_segment<LT>(a, b, L, ks, ke, w + b, g, lane, s_inv, s_p, s_alpha);
+    }
+    if (cn >= hi) break;                     // then b + 1 < batch, since cum[batch] >= hi
+    ++b;
+    cb = cn;
+  }
+}
+
+template <int LT>
 __global__ __launch_bounds__(kHeadDim) void decode_reduce_kernel(DecodeArgs a) {
   const int b = blockIdx.x / kQHeads;
   const int h = blockIdx.x % kQHeads;
   const int d = threadIdx.x;
-  const int n = min(visible_keys<LT>(a.seq_lens[b]), a.cache_cap);
-  const int ns = min((n + a.split_keys - 1) / a.split_keys, a.nsplit);
-  const size_t head0 = (size_t)b * a.nsplit * kQHeads + h;
+  const int C = a.ws_cum[a.batch];
+  const int cb = a.ws_cum[b];
+  const int cn = a.ws_cum[b + 1];
+  uint16_t* dst = a.out + ((size_t)b * kQHeads + h) * kHeadDim + d;
+  if (cn == cb) {                            // no visible key
+    *dst = 0;
+    return;
+  }
+  // Partitions touching the sequence: from the one holding its first chunk to the one
+  // holding its last; a partition with no chunk (only when C < P) wrote nothing.
+  const int w0 = part_of(cb, C, a.nparts);
+  const int w1 = part_of(cn - 1, C, a.nparts);
   float mx = -1e30f;
-  for (int s = 0; s < ns; ++s) mx = fmaxf(mx, a.ws_ml[(head0 + (size_t)s * kQHeads) * 2]);
+  for (int w = w0; w <= w1; ++w) {
+    if (part_lo(w, C, a.nparts) == part_lo(w + 1, C, a.nparts)) continue;
+    mx = fmaxf(mx, a.ws_ml[((size_t)(w + b) * kQHeads + h) * 2]);
+  }
   float den = 0.0f, num = 0.0f;
-  for (int s = 0; s < ns; ++s) {
-    const size_t hs = head0 + (size_t)s * kQHeads;
-    const float w = __builtin_amdgcn_exp2f(a.ws_ml[hs * 2] - mx);
-    den += w * a.ws_ml[hs * 2 + 1];
-    num += w * a.ws_o[hs * kHeadDim + d];
+  for (int w = w0; w <= w1; ++w) {
+    if (part_lo(w, C, a.nparts) == part_lo(w + 1, C, a.nparts)) continue;
+    const size_t hs = (size_t)(w + b) * kQHeads + h;
+    const float wt = __builtin_amdgcn_exp2f(a.ws_ml[hs * 2] - mx);
+    den += wt * a.ws_ml[hs * 2 + 1];
+    num += wt * a.ws_o[hs * kHeadDim + d];
   }
   const float gl = bf16_to_f32(a.gate[(size_t)b * kQHeads + h]);
   const float r = num / den * sigmoidf_fast(gl);
-  a.out[((size_t)b * kQHeads + h) * kHeadDim + d] = (uint16_t)(pack_bf16x2(r, 0.0f) & 0xffffu);
+  *dst = (uint16_t)(pack_bf16x2(r, 0.0f) & 0xffffu);
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Partitions chosen automatically: one per CU of the current device.  On MI355X (256 CUs)
+// one 4-wave workgroup per CU streams faster than two or more: fewer concurrent streams,
+// each reading 64 KB of consecutive K (and V) slots per step, keep HBM rows open longer,
+// and each extra partition adds a 16 KB partial result to write and merge.
+int auto_parts() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+    cus = 256;
+  return cus;
 }
 
 }  // namespace
 
-DecodePlan plan_decode(int layer_type, int batch, int max_seq_len, int split_keys) {
+DecodePlan plan_decode(int layer_type, int batch, int max_seq_len, int nparts) {
   DecodePlan p{};
   const int n = layer_type == kFull ? max_seq_len : (max_seq_len < kWindow ? max_seq_len : kWindow);
-  int sk = split_keys;
-  if (sk <= 0) {
-    // Aim for >= 2048 workgroups (8 per CU) without splits shorter than 256 keys.
-    sk = 4096;
-    while (sk > 256 && (long long)batch * ((n + sk - 1) / sk) < 2048) sk >>= 1;
-    if (layer_type == kSliding) sk = 128;
+  const long long max_chunks = (long long)batch * ((n + kChunk - 1) / kChunk);
+  int P = nparts;
+  if (P <= 0) {
+    const int want = auto_parts();
+    P = (int)(max_chunks < want ? max_chunks : want);
+    if (P < 1) P = 1;
   }
-  p.split_keys = sk;
-  p.nsplit = (n + sk - 1) / sk;
-  p.ws_o_bytes = (size_t)batch * p.nsplit * kQHeads * kHeadDim * sizeof(float);
-  p.ws_ml_bytes = (size_t)batch * p.nsplit * kQHeads * 2 * sizeof(float);
-  p.total_bytes = ((p.ws_o_bytes + 255) & ~(size_t)255) + p.ws_ml_bytes;
+  p.nparts = P;
+  p.cum_offset = 0;
+  p.first_offset = align256((size_t)(batch + 1) * sizeof(int32_t));
+  p.o_offset = p.first_offset + align256((size_t)P * sizeof(int32_t));
+  const size_t slots = (size_t)P + batch;
+  p.ml_offset = p.o_offset + align256(slots * kQHeads * kHeadDim * sizeof(float));
+  p.total_bytes = p.ml_offset + slots * kQHeads * 2 * sizeof(float);
   return p;
 }
 
 hipError_t launch_decode(int layer_type, const DecodeArgs& a, hipStream_t stream) {
-  const dim3 grid_split(a.nsplit, a.batch);
   const dim3 grid_reduce(a.batch * kQHeads);
   if (layer_type == kSliding) {
-    hipLaunchKernelGGL(decode_split_kernel<kSliding>, grid_split, dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL(decode_plan_kernel<kSliding>, dim3(1), dim3(kPlanThreads), 0, stream, a);
+    hipLaunchKernelGGL(decode_split_kernel<kSliding>, dim3(a.nparts), dim3(kThreads), 0, stream, a);
     hipLaunchKernelGGL(decode_reduce_kernel<kSliding>, grid_reduce, dim3(kHeadDim), 0, stream, a);
   } else {
-    hipLaunchKernelGGL(decode_split_kernel<kFull>, grid_split, dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL(decode_plan_kernel<kFull>, dim3(1), dim3(kPlanThreads), 0, stream, a);
+    hipLaunchKernelGGL(decode_split_kernel<kFull>, dim3(a.nparts), dim3(kThreads), 0, stream, a);
     hipLaunchKernelGGL(decode_reduce_kernel<kFull>, grid_reduce, dim3(kHeadDim), 0, stream, a);
   }
   return hipGetLastError();

@@ -38,13 +38,14 @@ struct DecodeArgs {
   const uint16_t* cache_k;
   const uint16_t* cache_v;
   const int32_t* seq_lens;
-  float* ws_o;            // [B, nsplit, 16, 256]
-  float* ws_ml;           // [B, nsplit, 16, 2]
+  int32_t* ws_cum;        // [B + 1] prefix sums of the per-sequence 32-key chunk counts
+  int32_t* ws_first;      // [P] sequence holding the first chunk of each partition
+  float* ws_o;            // [P + B, 16, 256] partial results, slot = partition + sequence
+  float* ws_ml;           // [P + B, 16, 2] (max, sum) per partial
   uint16_t* out;          // [B, 16, 256]
   int batch;
   int cache_cap;
-  int nsplit;
-  int split_keys;
+  int nparts;             // P
 };
 
 hipError_t launch_prefill(int layer_type, const PrefillArgs& a, hipStream_t stream);
@@ -54,13 +55,15 @@ hipError_t launch_decode(int layer_type, const DecodeArgs& a, hipStream_t stream
 int prefill_block_rows();
 
 // Decode planning, shared by the workspace query and the decode call.
+// Workspace regions are byte offsets from its start, each 256-byte aligned.
 struct DecodePlan {
-  int split_keys;
-  int nsplit;
-  size_t ws_o_bytes;
-  size_t ws_ml_bytes;
+  int nparts;
+  size_t cum_offset;
+  size_t first_offset;
+  size_t o_offset;
+  size_t ml_offset;
   size_t total_bytes;
 };
-DecodePlan plan_decode(int layer_type, int batch, int max_seq_len, int split_keys);
+DecodePlan plan_decode(int layer_type, int batch, int max_seq_len, int nparts);
 
 }  // namespace spark

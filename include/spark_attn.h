@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define SPARK_ATTN_ABI_VERSION 1
+#define SPARK_ATTN_ABI_VERSION 2
 
 enum { SPARK_Q_HEADS = 16, SPARK_KV_HEADS = 4, SPARK_HEAD_DIM = 256, SPARK_WINDOW = 512 };
 
@@ -112,12 +112,13 @@ spark_status spark_kv_append(int32_t layer_type, int32_t batch, int32_t n_new,
                              const spark_kv_cache* cache, void* stream);
 
 /*
- * Bytes of device workspace spark_attn_decode needs for this shape and split size
- * (split_keys = 0 lets the library choose, exactly as spark_attn_decode will).
- * Returns 0 for arguments spark_attn_decode would reject.
+ * Bytes of device workspace spark_attn_decode needs for this shape and partition count
+ * (num_parts = 0 lets the library choose, exactly as spark_attn_decode will).  The size
+ * grows with batch and num_parts only: (num_parts + batch) partial results of 16 x 258
+ * floats, plus the partition plan.  Returns 0 for arguments spark_attn_decode would reject.
  */
 size_t spark_attn_decode_workspace_bytes(int32_t layer_type, int32_t batch,
-                                         int32_t max_seq_len, int32_t split_keys);
+                                         int32_t max_seq_len, int32_t num_parts);
 
 /*
  * Decode: one query token per sequence against the layer's cache.
@@ -125,21 +126,25 @@ size_t spark_attn_decode_workspace_bytes(int32_t layer_type, int32_t batch,
  *   gate_logits  bf16 [batch, 16]
  *   cache        the layer's cache, already holding the current token
  *   seq_lens     device int32 [batch]: L = tokens in the cache including the current one,
- *                1 <= L <= max_seq_len
- *   max_seq_len  host upper bound of seq_lens (plans the split of the key sequence);
- *                FULL: <= capacity
- *   split_keys   keys per split (multiple of 64), or 0 for the library's choice
+ *                1 <= L <= max_seq_len (a sequence with L < 1 gets a zero output)
+ *   max_seq_len  host upper bound of seq_lens; FULL: <= capacity
+ *   num_parts    number of workgroups the batch's visible keys are divided among, in
+ *                equal runs of 32-key chunks across sequence boundaries (1 .. 2^20), or 0
+ *                for the library's choice; the result does not depend on it beyond rounding
  *   workspace    device scratch of at least spark_attn_decode_workspace_bytes(...)
- *                bytes, 256-byte aligned, used only during the call
+ *                bytes, 256-byte aligned, used only during the call (calls sharing one
+ *                workspace must be ordered on a stream)
  *   out          bf16 [batch, 16, 256] (written)
  * FULL layers read positions 0..L-1; SLIDING layers read positions max(0, L-512)..L-1
- * from the ring.  Two launches: split attention with per-split partial results, then a
- * log-sum-exp reduction that also applies the gate.
+ * from the ring (attention over a set of keys does not depend on their order).  Three
+ * launches: the partition plan (prefix sums of chunk counts, computed on the device),
+ * attention with per-(partition, sequence) partial results, then a log-sum-exp merge
+ * that also applies the gate.
  */
 spark_status spark_attn_decode(int32_t layer_type, int32_t batch, const void* q,
                                const void* gate_logits, const spark_kv_cache* cache,
                                const int32_t* seq_lens, int32_t max_seq_len,
-                               int32_t split_keys, void* workspace,
+                               int32_t num_parts, void* workspace,
                                size_t workspace_bytes, void* out, void* stream);
 
 /* Static description of a status code; never NULL. */

@@ -30,7 +30,7 @@ def test_exports_every_declared_function():
 
 
 def test_version_and_status_strings():
-    assert fga.abi_version() == 1
+    assert fga.abi_version() == 2
     assert fga.status_string(0) == "ok"
     assert fga.status_string(3) == "decode workspace too small"
     assert fga.status_string(99) == "unknown status"
@@ -67,19 +67,34 @@ def test_append_rejects():
     assert f(1, 1, 1, FAKE, FAKE, FAKE, None, None) == 1
 
 
+def _layout_bytes(batch, parts):
+    """The workspace layout the header documents: chunk prefix sums [batch + 1] and the first
+    sequence of each partition (int32), then (parts + batch) partials of 16 x 256 floats
+    and 16 x 2 floats, each region 256-byte aligned."""
+    up = lambda x: (x + 255) // 256 * 256
+    slots = parts + batch
+    return up(4 * (batch + 1)) + up(4 * parts) + up(slots * 16 * 256 * 4) + slots * 16 * 2 * 4
+
+
 def test_workspace_planning():
     ws = fga.decode_workspace_bytes
-    assert ws(1, 64, 32768) > 0
-    assert ws(1, 1, 64, 32) == 2 * 16 * 256 * 4 + 2 * 16 * 2 * 4
-    assert ws(0, 1, 100000, 32) == 16 * 16 * 256 * 4 + 16 * 16 * 2 * 4   # ring: <= 512 keys
-    assert ws(1, 1, 64, 33) == 0 and ws(2, 1, 64) == 0 and ws(1, 0, 64) == 0
+    assert ws(1, 1, 64, 2) == _layout_bytes(1, 2)
+    assert ws(1, 3, 64, 5000) == _layout_bytes(3, 5000)
+    # Library's choice: never more partitions than 32-key chunks in the batch, at most one
+    # per CU (256 on MI355X; the CPU test host has no device, so it plans for 256).
+    assert ws(1, 1, 64) == _layout_bytes(1, 2)
+    assert ws(0, 1, 100000) == _layout_bytes(1, 16)       # ring: <= 512 keys = 16 chunks
+    assert ws(1, 64, 32768) == _layout_bytes(64, 256)
+    assert ws(1, 1, 64, -1) == 0 and ws(1, 1, 64, (1 << 20) + 1) == 0
+    assert ws(2, 1, 64) == 0 and ws(1, 0, 64) == 0 and ws(1, 1, 0) == 0
 
 
 def test_decode_rejects():
     f = lib.spark_attn_decode
     big = 1 << 30
     assert f(1, 1, FAKE, FAKE, _cache(cap=64), FAKE, 65, 0, FAKE, big, FAKE, None) == 1   # > capacity
-    assert f(1, 1, FAKE, FAKE, _cache(cap=64), FAKE, 64, 48, FAKE, big, FAKE, None) == 1  # split % 32
-    assert f(1, 1, FAKE, FAKE, _cache(cap=64), FAKE, 64, 32, FAKE, 16, FAKE, None) == 3   # workspace
+    assert f(1, 1, FAKE, FAKE, _cache(cap=64), FAKE, 64, -1, FAKE, big, FAKE, None) == 1  # parts < 0
+    assert f(1, 1, FAKE, FAKE, _cache(cap=64), FAKE, 64, (1 << 20) + 1, FAKE, big, FAKE, None) == 1
+    assert f(1, 1, FAKE, FAKE, _cache(cap=64), FAKE, 64, 2, FAKE, 16, FAKE, None) == 3    # workspace
     assert f(1, 1, FAKE, FAKE, _cache(cap=64), FAKE, 64, 0, MISALIGNED, big, FAKE, None) == 1
     assert f(0, 1, FAKE, FAKE, _cache(cap=1024), FAKE, 64, 0, FAKE, big, FAKE, None) == 1

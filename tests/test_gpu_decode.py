@@ -31,13 +31,13 @@ def _ring_from_contiguous(ck, cv, lens):
     return rk, rv
 
 
-def _decode_dev(fga, lt, d, ck, cv, lens, split_keys=0, max_len=None):
+def _decode_dev(fga, lt, d, ck, cv, lens, num_parts=0, max_len=None):
     import torch
     B = len(lens)
     cap = ck.shape[1]
     cache = fga.KVCache(lt, B, cap, k=to_dev(ck), v=to_dev(cv))
     out = fga.decode(lt, to_dev(d["q"]), to_dev(d["gate"]), cache, i32_dev(lens),
-                     int(max(lens)) if max_len is None else max_len, split_keys=split_keys)
+                     max(1, int(max(lens))) if max_len is None else max_len, num_parts=num_parts)
     torch.cuda.synchronize()
     return f64_of(out)
 
@@ -46,28 +46,45 @@ EDGE = [[1], [5], [511], [512], [513], [1, 37, 600, 1025], [4097, 64, 2000]]
 
 
 @pytest.mark.parametrize("lens", EDGE, ids=["L" + "-".join(map(str, x)) for x in EDGE])
-@pytest.mark.parametrize("split_keys", [0, 32, 96, 4096])
-def test_decode_edges_both_types(fga, lens, split_keys):
+@pytest.mark.parametrize("num_parts", [0, 1, 3, 64, 5000])
+def test_decode_edges_both_types(fga, lens, num_parts):
+    """Partition counts from one workgroup for the whole batch to far more workgroups than
+    32-key chunks (most then hold no chunk), so partitions start and end mid-sequence, at
+    sequence boundaries and inside ragged last chunks."""
     lens = np.array(lens, np.int32)
     B, cap = len(lens), int(lens.max())
     d = synth.decode_inputs(4000 + int(lens.sum()), B, cap, fill_lens=lens)
-    note(f"decode edges lens={lens.tolist()} split={split_keys}")
-    got = _decode_dev(fga, oracle.FULL, d, d["cache_k"], d["cache_v"], lens, split_keys)
+    note(f"decode edges lens={lens.tolist()} parts={num_parts}")
+    got = _decode_dev(fga, oracle.FULL, d, d["cache_k"], d["cache_v"], lens, num_parts)
     want = oracle.decode(d["q"], d["gate"], d["cache_k"], d["cache_v"], lens, oracle.FULL)
-    assert_parity(got, want, f"decode full lens={lens.tolist()} split={split_keys}")
-    if split_keys in (0, 32, 96):
-        rk, rv = _ring_from_contiguous(d["cache_k"], d["cache_v"], lens)
-        got = _decode_dev(fga, oracle.SLIDING, d, rk, rv, lens, split_keys)
-        want = oracle.decode(d["q"], d["gate"], rk, rv, lens, oracle.SLIDING)
-        assert_parity(got, want, f"decode sliding lens={lens.tolist()} split={split_keys}")
+    assert_parity(got, want, f"decode full lens={lens.tolist()} parts={num_parts}")
+    rk, rv = _ring_from_contiguous(d["cache_k"], d["cache_v"], lens)
+    got = _decode_dev(fga, oracle.SLIDING, d, rk, rv, lens, num_parts)
+    want = oracle.decode(d["q"], d["gate"], rk, rv, lens, oracle.SLIDING)
+    assert_parity(got, want, f"decode sliding lens={lens.tolist()} parts={num_parts}")
 
 
-def test_split_count_does_not_change_result(fga):
-    lens = np.array([3000, 1500], np.int32)
-    d = synth.decode_inputs(4100, 2, 3000, fill_lens=lens)
-    outs = [_decode_dev(fga, oracle.FULL, d, d["cache_k"], d["cache_v"], lens, sk) for sk in (32, 256, 2048, 4096)]
+def test_partition_count_does_not_change_result(fga):
+    lens = np.array([3000, 1500, 33, 4000], np.int32)
+    d = synth.decode_inputs(4100, 4, 4000, fill_lens=lens)
+    outs = [_decode_dev(fga, oracle.FULL, d, d["cache_k"], d["cache_v"], lens, p)
+            for p in (1, 7, 256, 2048)]
     for o in outs[1:]:
         assert np.max(np.abs(o - outs[0])) < 4e-3
+
+
+@pytest.mark.parametrize("num_parts", [0, 2, 40])
+def test_decode_zero_length_sequences(fga, num_parts):
+    """A sequence with L = 0 sees no key and gets a zero output; its neighbours are unaffected."""
+    lens = np.array([0, 70, 0, 0, 33, 0], np.int32)
+    B, cap = len(lens), 128
+    d = synth.decode_inputs(4200, B, cap, fill_lens=lens)
+    got = _decode_dev(fga, oracle.FULL, d, d["cache_k"], d["cache_v"], lens, num_parts, max_len=cap)
+    live = lens > 0
+    assert np.all(got[~live] == 0.0)
+    want = oracle.decode(d["q"][live], d["gate"][live], d["cache_k"][live], d["cache_v"][live],
+                         lens[live], oracle.FULL)
+    assert_parity(got[live], want, f"decode with empty sequences parts={num_parts}")
 
 
 def test_config3_batched_decode(fga):
@@ -175,5 +192,5 @@ def test_decode_rejects_small_workspace(fga):
     g = torch.zeros(1, 16, dtype=torch.bfloat16, device="cuda")
     ws = torch.empty(256, dtype=torch.uint8, device="cuda")
     with pytest.raises(fga.SparkError) as e:
-        fga.decode(oracle.FULL, q, g, cache, i32_dev([64]), 64, workspace=ws, split_keys=32)
+        fga.decode(oracle.FULL, q, g, cache, i32_dev([64]), 64, workspace=ws, num_parts=2)
     assert e.value.status == 3
