@@ -21,7 +21,8 @@
 //       - O += P V on the VALU in fp32: V rows are loaded fully coalesced (two 512-byte
 //         rows per instruction), each lane owns 8 dims of one key parity, P from LDS.
 //   * merge: per (sequence, query head), the partials of the partitions that touched the
-//     sequence are combined with log-sum-exp weights and the sigmoid head gate is applied.
+//     sequence (a range the plan records) are combined with log-sum-exp weights and the
+//     sigmoid head gate is applied.
 // Sliding layers read the 512-slot ring; full layers the contiguous cache.
 #include "spark_device.hpp"
 #include "spark_launch.hpp"
@@ -73,15 +74,20 @@ __global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(DecodeArgs a)
     __syncthreads();
   }
   const int C = s_scan[kPlanThreads - 1];
+  const int P = min(a.nparts, C);            // so that no partition is empty
   int run = s_scan[t] - own;
   for (int b = b0; b < b1; ++b) {
     const int c = chunks_of<LT>(a.seq_lens[b], a.cache_cap);
     a.ws_cum[b] = run;
     if (c > 0) {
       // Partitions whose first chunk falls in [run, run + c) start in sequence b.
-      const int w0 = (int)(((long long)run * a.nparts + C - 1) / C);
-      const int w1 = (int)(((long long)(run + c) * a.nparts + C - 1) / C);
+      const int w0 = (int)(((long long)run * P + C - 1) / C);
+      const int w1 = (int)(((long long)(run + c) * P + C - 1) / C);
       for (int w = w0; w < w1; ++w) a.ws_first[w] = b;
+      // Partitions touching b: those holding its first and its last chunk, and all between.
+      a.ws_range[b] = int2{part_of(run, C, P), part_of(run + c - 1, C, P)};
+    } else {
+      a.ws_range[b] = int2{0, -1};
     }
     run += c;
   }
@@ -248,9 +254,10 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
 
   const int w = blockIdx.x;
   const int C = a.ws_cum[a.batch];
-  const int lo = part_lo(w, C, a.nparts);
-  const int hi = part_lo(w + 1, C, a.nparts);
-  if (lo >= hi) return;                      // uniform over the workgroup
+  const int P = min(a.nparts, C);            // as planned: every partition below P has chunks
+  if (w >= P) return;                        // uniform over the workgroup
+  const int lo = part_lo(w, C, P);
+  const int hi = part_lo(w + 1, C, P);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -275,39 +282,32 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
   }
 }
 
-template <int LT>
-__global__ __launch_bounds__(kHeadDim) void decode_reduce_kernel(DecodeArgs a) {
+// One wave per (sequence, query head); lane l owns dims 4l..4l+3.  The partials are
+// merged in one online pass: running max, rescaled sum and rescaled output.
+__global__ __launch_bounds__(64) void decode_reduce_kernel(DecodeArgs a) {
   const int b = blockIdx.x / kQHeads;
   const int h = blockIdx.x % kQHeads;
-  const int d = threadIdx.x;
-  const int C = a.ws_cum[a.batch];
-  const int cb = a.ws_cum[b];
-  const int cn = a.ws_cum[b + 1];
-  uint16_t* dst = a.out + ((size_t)b * kQHeads + h) * kHeadDim + d;
-  if (cn == cb) {                            // no visible key
-    *dst = 0;
-    return;
-  }
-  // Partitions touching the sequence: from the one holding its first chunk to the one
-  // holding its last; a partition with no chunk (only when C < P) wrote nothing.
-  const int w0 = part_of(cb, C, a.nparts);
-  const int w1 = part_of(cn - 1, C, a.nparts);
-  float mx = -1e30f;
-  for (int w = w0; w <= w1; ++w) {
-    if (part_lo(w, C, a.nparts) == part_lo(w + 1, C, a.nparts)) continue;
-    mx = fmaxf(mx, a.ws_ml[((size_t)(w + b) * kQHeads + h) * 2]);
-  }
-  float den = 0.0f, num = 0.0f;
-  for (int w = w0; w <= w1; ++w) {
-    if (part_lo(w, C, a.nparts) == part_lo(w + 1, C, a.nparts)) continue;
+  const int lane = threadIdx.x;
+  const int2 r = a.ws_range[b];
+  float m = -1e30f, l = 0.0f;
+  f32x4 o = f32x4{0, 0, 0, 0};
+#pragma unroll 4
+  for (int w = r.x; w <= r.y; ++w) {
     const size_t hs = (size_t)(w + b) * kQHeads + h;
-    const float wt = __builtin_amdgcn_exp2f(a.ws_ml[hs * 2] - mx);
-    den += wt * a.ws_ml[hs * 2 + 1];
-    num += wt * a.ws_o[hs * kHeadDim + d];
+    const float2 ml = *reinterpret_cast<const float2*>(a.ws_ml + hs * 2);
+    const f32x4 ow = *reinterpret_cast<const f32x4*>(a.ws_o + hs * kHeadDim + 4 * lane);
+    const float mn = fmaxf(m, ml.x);
+    const float sa = __builtin_amdgcn_exp2f(m - mn);
+    const float sb = __builtin_amdgcn_exp2f(ml.x - mn);
+    l = l * sa + ml.y * sb;
+    o = o * sa + ow * sb;
+    m = mn;
   }
+  // No visible key (r empty): l = 0 and o = 0, written as zeros.
   const float gl = bf16_to_f32(a.gate[(size_t)b * kQHeads + h]);
-  const float r = num / den * sigmoidf_fast(gl);
-  *dst = (uint16_t)(pack_bf16x2(r, 0.0f) & 0xffffu);
+  const float sc = l > 0.0f ? sigmoidf_fast(gl) / l : 0.0f;
+  uint16_t* dst = a.out + ((size_t)b * kQHeads + h) * kHeadDim + 4 * lane;
+  *reinterpret_cast<u32x2*>(dst) = u32x2{pack_bf16x2(o[0] * sc, o[1] * sc), pack_bf16x2(o[2] * sc, o[3] * sc)};
 }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -338,7 +338,8 @@ DecodePlan plan_decode(int layer_type, int batch, int max_seq_len, int nparts) {
   }
   p.nparts = P;
   p.cum_offset = 0;
-  p.first_offset = align256((size_t)(batch + 1) * sizeof(int32_t));
+  p.range_offset = align256((size_t)(batch + 1) * sizeof(int32_t));
+  p.first_offset = p.range_offset + align256((size_t)batch * 2 * sizeof(int32_t));
   p.o_offset = p.first_offset + align256((size_t)P * sizeof(int32_t));
   const size_t slots = (size_t)P + batch;
   p.ml_offset = p.o_offset + align256(slots * kQHeads * kHeadDim * sizeof(float));
@@ -351,11 +352,11 @@ hipError_t launch_decode(int layer_type, const DecodeArgs& a, hipStream_t stream
   if (layer_type == kSliding) {
     hipLaunchKernelGGL(decode_plan_kernel<kSliding>, dim3(1), dim3(kPlanThreads), 0, stream, a);
     hipLaunchKernelGGL(decode_split_kernel<kSliding>, dim3(a.nparts), dim3(kThreads), 0, stream, a);
-    hipLaunchKernelGGL(decode_reduce_kernel<kSliding>, grid_reduce, dim3(kHeadDim), 0, stream, a);
+    hipLaunchKernelGGL(decode_reduce_kernel, grid_reduce, dim3(64), 0, stream, a);
   } else {
     hipLaunchKernelGGL(decode_plan_kernel<kFull>, dim3(1), dim3(kPlanThreads), 0, stream, a);
     hipLaunchKernelGGL(decode_split_kernel<kFull>, dim3(a.nparts), dim3(kThreads), 0, stream, a);
-    hipLaunchKernelGGL(decode_reduce_kernel<kFull>, grid_reduce, dim3(kHeadDim), 0, stream, a);
+    hipLaunchKernelGGL(decode_reduce_kernel, grid_reduce, dim3(64), 0, stream, a);
   }
   return hipGetLastError();
 }
