@@ -47,7 +47,9 @@ def _load():
     lib = ctypes.CDLL(_LIB_PATH)
     i32, vp, sz = ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t
     cache_p = ctypes.POINTER(KvCacheDesc)
-    lib.spark_attn_prefill.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp, cache_p, vp, vp]
+    lib.spark_attn_prefill_workspace_bytes.argtypes = [i32, i32, i32]
+    lib.spark_attn_prefill_workspace_bytes.restype = sz
+    lib.spark_attn_prefill.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp, cache_p, vp, sz, vp, vp]
     lib.spark_attn_prefill.restype = i32
     lib.spark_kv_append.argtypes = [i32, i32, i32, vp, vp, vp, cache_p, vp]
     lib.spark_kv_append.restype = i32
@@ -65,7 +67,7 @@ def _load():
 _lib = _load()
 
 LIBRARY_PATH = _LIB_PATH
-EXPORTED = ("spark_attn_prefill", "spark_kv_append", "spark_attn_decode_workspace_bytes",
+EXPORTED = ("spark_attn_prefill_workspace_bytes", "spark_attn_prefill", "spark_kv_append", "spark_attn_decode_workspace_bytes",
             "spark_attn_decode", "spark_status_string", "spark_abi_version")
 
 
@@ -133,9 +135,14 @@ class KVCache:
         return KvCacheDesc(self.k.data_ptr(), self.v.data_ptr(), self.batch, self.capacity)
 
 
+def prefill_workspace_bytes(layer_type: int, batch: int, seq_len: int) -> int:
+    return int(_lib.spark_attn_prefill_workspace_bytes(int(layer_type), int(batch), int(seq_len)))
+
+
 def prefill(layer_type: int, q, k, v, gate, out=None, cache: KVCache | None = None,
-            start_pos: int = 0, stream=None):
-    """spark_attn_prefill: q [B,S,16,256], k/v [B,S,4,256], gate [B,S,16] (bf16, pre-RoPE)."""
+            start_pos: int = 0, workspace=None, stream=None):
+    """spark_attn_prefill: q [B,S,16,256], k/v [B,S,4,256], gate [B,S,16] (bf16, pre-RoPE);
+    ``workspace`` (uint8, >= prefill_workspace_bytes) is allocated per call when omitted."""
     torch = _torch()
     B, S = int(q.shape[0]), int(q.shape[1])
     _check(q, "q", (B, S, N_Q_HEADS, HEAD_DIM), torch.bfloat16)
@@ -150,8 +157,13 @@ def prefill(layer_type: int, q, k, v, gate, out=None, cache: KVCache | None = No
         if cache.layer_type != layer_type:
             raise ValueError("cache layer type differs from the call's")
         desc = ctypes.pointer(cache.desc())
+    if workspace is None:
+        need = prefill_workspace_bytes(layer_type, B, S)
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    _check(workspace, "workspace", None, torch.uint8)
     st = _lib.spark_attn_prefill(int(layer_type), B, S, int(start_pos), _ptr(q), _ptr(k), _ptr(v),
-                                 _ptr(gate), desc, _ptr(out), _stream(stream))
+                                 _ptr(gate), desc, _ptr(workspace), int(workspace.numel()),
+                                 _ptr(out), _stream(stream))
     if st:
         raise SparkError(st, "spark_attn_prefill")
     return out

@@ -1,5 +1,5 @@
 // extern "C" entry points declared in include/spark_attn.h: host-side argument checks,
-// then one launch (prefill, append) or two (decode) on the caller's stream.  Every check
+// then the launches (prefill two, append one, decode three) on the caller's stream.  Every check
 // runs before any HIP call, so a rejected call enqueues nothing and touches no device.
 #include "spark_attn.h"
 #include "spark_device.hpp"
@@ -36,18 +36,29 @@ const char* spark_status_string(int32_t s) {
     case SPARK_OK: return "ok";
     case SPARK_ERR_INVALID_ARG: return "invalid argument";
     case SPARK_ERR_UNSUPPORTED: return "unsupported request";
-    case SPARK_ERR_WORKSPACE: return "decode workspace too small";
+    case SPARK_ERR_WORKSPACE: return "workspace too small";
     case SPARK_ERR_HIP: return "HIP launch failure";
     default: return "unknown status";
   }
 }
 
+size_t spark_attn_prefill_workspace_bytes(int32_t layer_type, int32_t batch, int32_t seq_len) {
+  if (!valid_type(layer_type) || batch < 1 || batch > kMaxBatch || seq_len < 1 || seq_len > kMaxSeq ||
+      (long long)batch * seq_len > 0xfffffffeLL)
+    return 0;
+  return spark::prefill_workspace_bytes(batch, seq_len);
+}
+
 spark_status spark_attn_prefill(int32_t layer_type, int32_t batch, int32_t seq_len,
                                 int32_t start_pos, const void* q, const void* k,
                                 const void* v, const void* gate_logits,
-                                const spark_kv_cache* cache, void* out, void* stream) {
+                                const spark_kv_cache* cache, void* workspace,
+                                size_t workspace_bytes, void* out, void* stream) {
   if (!valid_type(layer_type)) return SPARK_ERR_INVALID_ARG;
   if (batch < 1 || batch > kMaxBatch || seq_len < 1 || seq_len > kMaxSeq) return SPARK_ERR_INVALID_ARG;
+  // The RoPE pass runs one thread per 16-byte K chunk, 128 per token, 256 per workgroup;
+  // the attention grid has ceil(seq_len / 48) * batch * 4 workgroups.
+  if ((long long)batch * seq_len > 0xfffffffeLL) return SPARK_ERR_INVALID_ARG;
   if (!q || !k || !v || !gate_logits || !out) return SPARK_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned2(gate_logits))
     return SPARK_ERR_INVALID_ARG;
@@ -58,14 +69,16 @@ spark_status spark_attn_prefill(int32_t layer_type, int32_t batch, int32_t seq_l
     if (cs != SPARK_OK) return cs;
     if (layer_type == SPARK_LAYER_FULL && cache->capacity < seq_len) return SPARK_ERR_INVALID_ARG;
   }
+  if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u)) return SPARK_ERR_INVALID_ARG;
+  if (workspace_bytes < spark::prefill_workspace_bytes(batch, seq_len)) return SPARK_ERR_WORKSPACE;
   const int rows = spark::prefill_block_rows();
   const long long nqb = (seq_len + rows - 1) / rows;
-  if (nqb * batch * SPARK_KV_HEADS > 0x7fffffffLL) return SPARK_ERR_INVALID_ARG;
 
   spark::PrefillArgs a{};
   a.q = static_cast<const uint16_t*>(q);
   a.k = static_cast<const uint16_t*>(k);
   a.v = static_cast<const uint16_t*>(v);
+  a.k_rot = static_cast<uint16_t*>(workspace);
   a.gate = static_cast<const uint16_t*>(gate_logits);
   a.out = static_cast<uint16_t*>(out);
   a.cache_k = cache ? static_cast<uint16_t*>(cache->k) : nullptr;

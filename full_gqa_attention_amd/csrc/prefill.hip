@@ -1,18 +1,20 @@
 // Flash-attention prefill for the hybrid sliding/full GQA layer on gfx950.
 //
-// One workgroup = 4 waves (one per SIMD) = one KV head g of one sequence and a block of
-// 64 query positions; wave w computes query head 4g + w for all 64 positions as two
-// 32-row blocks.  Every K/V tile in LDS thus serves 4 query heads x 64 positions (GQA
-// sharing), and every MFMA operand read from LDS feeds two MFMAs (one per row block).
-// With one wave per SIMD a wave may hold 512 registers: the two 32x256 fp32 output
-// accumulators live in AGPRs, the rotated Q fragments of both blocks in VGPRs.
+// Two launches.  First a streaming pass applies RoPE to K once per position (into the
+// caller's workspace) and writes the rotated keys and the values into the KV cache when
+// one is given.  Then the attention kernel:
+//
+// One workgroup = 8 waves (two per SIMD) = one KV head g of one sequence and a block of
+// 64 query positions; wave w computes query head 4g + w/2 for 32 of the positions.  Every
+// K/V tile in LDS thus serves 4 query heads x 64 positions (GQA sharing).  Two waves per
+// SIMD let one wave's MFMAs run while the other waits on LDS reads or transcendentals:
+// measured on gfx950, each LDS read or exp interleaved into a single wave's MFMA stream
+// costs that stream about 11-17 cycles.
 //
 // K/V tiles of 32 keys stream through a 3-stage LDS ring filled by direct global->LDS
 // loads (no register staging), issued two tiles ahead:
-//   * K tile, chunk-major (16-byte chunk c of key j at slot 32c + j): the MFMA A operand
-//     of S^T = K Q^T is one conflict-free 16-byte read.  RoPE is applied in place by the
-//     lane that loaded a rotary pair of chunks (m, m + r/2), right after its own load
-//     lands; on full layers only two waves hold rotary chunks.
+//   * K tile (already rotated), chunk-major (16-byte chunk c of key j at slot 32c + j): the
+//     MFMA A operand of S^T = K Q^T is one conflict-free 16-byte read.
 //   * V tile, row-major with the chunk index XOR-swizzled by 4 * (row % 4): the A operand
 //     of O^T += V^T P^T (V transposed) comes from two ds_read_b64_tr_b16 per MFMA, which
 //     transpose 16-bit elements across each group of 16 lanes.
@@ -24,9 +26,7 @@
 // Sliding layers visit only the 512-key band (Spark-X2.6-4B-Base hybrid attention
 // explainer, eliteato.com/news/34565, section "滑动窗口 512"); full layers every earlier
 // key (section "36 层混合注意力排布").  Epilogue: O / l * sigmoid(gate) (F16 vs Q4
-// comparison page, hotelren.com/news/5475707, section 三), stored as bf16.  The
-// workgroup owning a key tile's positions also writes its rotated keys and values into
-// the KV cache.
+// comparison page, hotelren.com/news/5475707, section 三), stored as bf16.
 #include "spark_device.hpp"
 #include "spark_launch.hpp"
 
@@ -66,41 +66,23 @@ __device__ __forceinline__ void barrier_lds() {
   __builtin_amdgcn_s_barrier();
 }
 
-// The K tile is filled by 16 load instructions; instruction n brings chunks 2n and 2n+1
-// of all 32 keys.  k_instr(w, q) is the q-th (of 4) that wave w issues, chosen so that a
-// rotary pair of chunks lands in one lane: instructions q = 0, 1 form one pair and
-// q = 2, 3 another.
-template <int LT>
-__device__ __forceinline__ int k_instr(int w, int q) {
-  if (kWaves == 4) {
-    if (LT == kSliding) return w + 4 * (q >> 1) + 8 * (q & 1);   // chunks c, c+16: dims d, d+128
-    if (w < 2) return q < 2 ? w + 2 * q : 4 + 2 * w + (q - 2);   // chunks c, c+4 (d < 32), then plain
-    return 8 + 4 * (w - 2) + q;                                  // chunks 16..31: plain
-  }
-  if (LT == kSliding) return w + 8 * q;                          // chunks c, c+16
-  if (w < 2) return w + 2 * q;                                   // chunks c, c+4 (d < 32)
-  return 2 * w + q;                                              // chunks 8..31: plain
-}
-
 constexpr int kKLoads = 16 / kWaves;              // K-tile load instructions per wave
 constexpr int kVLoads = 16 / kWaves;              // V-tile load instructions per wave
 
-template <int LT>
-__device__ __forceinline__ int k_rotary_pairs(int w) {         // rotary chunk pairs per lane
-  return LT == kSliding ? kKLoads / 2 : (w < 2 ? 1 : 0);
-}
-
-template <int LT>
+// Start loading tile (keys k0 .. k0+31) of (sequence b, KV head g): K from the rotated
+// keys.  Instruction n of K brings chunks 2n, 2n+1 of all 32 keys; instruction n of V rows
+// 2n, 2n+1 with chunk positions swizzled by 4 * (row % 4).  Rows past the end load row
+// S-1 (masked later).
 __device__ __forceinline__ void issue_tile(const PrefillArgs& a, int b, int g, int k0, int wave,
                                            int lane, uint8_t* ks, uint8_t* vs) {
   const int S = a.seq_len;
   const size_t seq_row0 = (size_t)b * S;
-  const int pk = min(k0 + (lane & 31), S - 1);      // rows past the end: any valid row (masked)
+  const int pk = min(k0 + (lane & 31), S - 1);
 #pragma unroll
   for (int q = 0; q < kKLoads; ++q) {
-    const int n = k_instr<LT>(wave, q);
+    const int n = kKLoads * wave + q;
     const int chunk = 2 * n + (lane >> 5);
-    dma16(a.k + ((seq_row0 + pk) * kKvHeads + g) * kHeadDim + 8 * chunk, ks + n * 1024);
+    dma16(a.k_rot + ((seq_row0 + pk) * kKvHeads + g) * kHeadDim + 8 * chunk, ks + n * 1024);
   }
 #pragma unroll
   for (int q = 0; q < kVLoads; ++q) {
@@ -112,53 +94,52 @@ __device__ __forceinline__ void issue_tile(const PrefillArgs& a, int b, int g, i
   }
 }
 
-// After this lane's loads of a tile have landed: rotate its rotary K chunk pairs in
-// place and, for the tiles of this workgroup's own positions, copy its K/V chunks to the
-// cache.
+// RoPE of K, once per position: k_rot = R_p(k) (rotate-half form: pair (m, m + r/2) is
+// rotated by angle p * theta^(-2m/r) for m < r/2; dims >= r are copied), and, when a cache
+// is given, the rotated keys and the values into their cache slots (full layer: slot p;
+// sliding layer: slot p mod 512 for the last 512 positions) -- Spark-X2.6-4B-Base hybrid
+// attention explainer, eliteato.com/news/34565, sections "全局注意力 5M 基频 RoPE" and
+// "滑动窗口 512".  One thread per 16-byte chunk of a K row: a rotary chunk also reads its
+// partner chunk (dims + or - r/2) and computes its own half of the pair.
 template <int LT>
-__device__ __forceinline__ void finish_tile(const PrefillArgs& a, int b, int g, int k0, int q0,
-                                            int wave, int lane, uint8_t* ks, uint8_t* vs,
-                                            const double* inv, bool& stored) {
-  const int S = a.seq_len;
-  const int key = lane & 31;
-  const int p = k0 + key;
-  const int npairs = k_rotary_pairs<LT>(wave);
+__global__ __launch_bounds__(256) void prefill_rope_kernel(PrefillArgs a) {
+  using T = LayerTraits<LT>;
+  constexpr int kHalf = T::kRot / 16;                // chunks in the first half of the rotary span
+  __shared__ double s_inv[T::kRot / 2];
+  if (threadIdx.x < T::kRot / 2) s_inv[threadIdx.x] = rope_inv_rev(threadIdx.x, T::kRot, log2(T::kTheta));
+  __syncthreads();
+  const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const size_t nrows = (size_t)a.batch * a.seq_len * kKvHeads;
+  const size_t row = idx >> 5;                       // (b * S + p) * 4 + g
+  const int c = (int)(idx & 31);
+  if (row >= nrows) return;
+  const int p = (int)((row / kKvHeads) % a.seq_len);
+  const uint16_t* krow = a.k + row * kHeadDim;
+  const u32x4 x = ld_global16(krow + 8 * c);
+  u32x4 y = x;
+  if (c < 2 * kHalf) {
+    const bool first = c < kHalf;
+    const u32x4 xp = ld_global16(krow + 8 * (first ? c + kHalf : c - kHalf));
+    const int m0 = 8 * (first ? c : c - kHalf);
 #pragma unroll
-  for (int pr = 0; pr < kKLoads / 2; ++pr) {
-    if (pr < npairs) {
-      const int na = k_instr<LT>(wave, 2 * pr), nb = k_instr<LT>(wave, 2 * pr + 1);
-      u32x4* pa = reinterpret_cast<u32x4*>(ks + na * 1024 + lane * 16);
-      u32x4* pb = reinterpret_cast<u32x4*>(ks + nb * 1024 + lane * 16);
-      u32x4 xa = *pa, xb = *pb;
-      rope_rotate_chunks(xa, xb, (double)p, inv, 8 * (2 * na + (lane >> 5)));
-      *pa = xa;
-      *pb = xb;
+    for (int w = 0; w < 4; ++w) {
+      float c0, s0, c1, s1;
+      rope_cos_sin((double)p, s_inv[m0 + 2 * w], c0, s0);
+      rope_cos_sin((double)p, s_inv[m0 + 2 * w + 1], c1, s1);
+      const float a0 = bf16_lo(x[w]), a1 = bf16_hi(x[w]);
+      const float b0 = bf16_lo(xp[w]), b1 = bf16_hi(xp[w]);
+      y[w] = first ? pack_bf16x2(a0 * c0 - b0 * s0, a1 * c1 - b1 * s1)
+                   : pack_bf16x2(a0 * c0 + b0 * s0, a1 * c1 + b1 * s1);
     }
   }
-  if (a.cache_k != nullptr && k0 >= q0) {
-    stored = true;
-    const int cap = a.cache_cap;
-    if (p < S && (LT == kFull || p >= S - kWindow)) {
-      const int slot = (LT == kFull) ? p : (p & (kWindow - 1));
-      uint16_t* dst = a.cache_k + (((size_t)b * cap + slot) * kKvHeads + g) * kHeadDim;
-#pragma unroll
-      for (int q = 0; q < kKLoads; ++q) {
-        const int n = k_instr<LT>(wave, q);
-        st_global16(dst + 8 * (2 * n + (lane >> 5)), *reinterpret_cast<const u32x4*>(ks + n * 1024 + lane * 16));
-      }
-    }
-#pragma unroll
-    for (int q = 0; q < kVLoads; ++q) {
-      const int n = kVLoads * wave + q;
-      const int r = 2 * n + (lane >> 5);
-      const int pv = k0 + r;
-      if (pv < S && (LT == kFull || pv >= S - kWindow)) {
-        const int chunk = (lane & 31) ^ (4 * (r & 3));
-        const int slot = (LT == kFull) ? pv : (pv & (kWindow - 1));
-        uint16_t* dst = a.cache_v + (((size_t)b * cap + slot) * kKvHeads + g) * kHeadDim;
-        st_global16(dst + 8 * chunk, *reinterpret_cast<const u32x4*>(vs + n * 1024 + lane * 16));
-      }
-    }
+  st_global16(a.k_rot + row * kHeadDim + 8 * c, y);
+  if (a.cache_k != nullptr && (LT == kFull || p >= a.seq_len - kWindow)) {
+    const int slot = LT == kFull ? p : (p & (kWindow - 1));
+    const size_t b = row / ((size_t)kKvHeads * a.seq_len);
+    const int g = (int)(row % kKvHeads);
+    const size_t dst = (((size_t)b * a.cache_cap + slot) * kKvHeads + g) * kHeadDim + 8 * c;
+    st_global16(a.cache_k + dst, y);
+    st_global16(a.cache_v + dst, ld_global16(a.v + row * kHeadDim + 8 * c));
   }
 }
 
@@ -263,8 +244,8 @@ void prefill_kernel(PrefillArgs a) {
   const int kt_hi = hi_key / kBN;
 
   // Start streaming the first two tiles before anything else.
-  issue_tile<LT>(a, b, g, kt_lo * kBN, wave, lane, s_k0, s_v0);
-  if (kt_lo + 1 <= kt_hi) issue_tile<LT>(a, b, g, (kt_lo + 1) * kBN, wave, lane, s_k1, s_v1);
+  issue_tile(a, b, g, kt_lo * kBN, wave, lane, s_k0, s_v0);
+  if (kt_lo + 1 <= kt_hi) issue_tile(a, b, g, (kt_lo + 1) * kBN, wave, lane, s_k1, s_v1);
 
   if (tid < T::kRot / 2) s_inv[tid] = rope_inv_rev(tid, T::kRot, log2(T::kTheta));
   barrier_lds();
@@ -274,12 +255,10 @@ void prefill_kernel(PrefillArgs a) {
 #pragma unroll
   for (int rb = 0; rb < kRowBlocks; ++rb) load_q<LT>(a, b, hq, q0 + 32 * (rb0 + rb) + r32, half, s_inv, qf[rb]);
 
-  // First tile: wait for this lane's loads, rotate, publish.  Waiting for the second
-  // tile too leaves no load in flight on entry to the loop, which lets the compiler keep
-  // exact track of the loads in flight per stage inside it.
-  bool stored = false;
+  // First tile: wait for this lane's loads, publish.  Waiting for the second tile too
+  // leaves no load in flight on entry to the loop, which lets the compiler keep exact
+  // track of the loads in flight per stage inside it.
   wait_vmcnt<0>();
-  finish_tile<LT>(a, b, g, kt_lo * kBN, q0, wave, lane, s_k0, s_v0, s_inv, stored);
   barrier_lds();
 
   f32x16 o[kRowBlocks][8];
@@ -314,7 +293,7 @@ void prefill_kernel(PrefillArgs a) {
     // The compiler cannot follow per-stage loads across the loop back edge, so the first
     // LDS read of step 0 waits for every load in flight; step 0 therefore starts its
     // prefetch after its MFMAs, the other steps before theirs.
-    if (ST != 0 && two_ahead) issue_tile<LT>(a, b, g, k0 + 2 * kBN, wave, lane, ks2, vs2);
+    if (ST != 0 && two_ahead) issue_tile(a, b, g, k0 + 2 * kBN, wave, lane, ks2, vs2);
 
     // Which row blocks see any key of this tile (wave-uniform).
     bool any[kRowBlocks], edge[kRowBlocks], any_rb = false;
@@ -387,13 +366,12 @@ void prefill_kernel(PrefillArgs a) {
         }
       }
     }
-    if (ST == 0 && two_ahead) issue_tile<LT>(a, b, g, k0 + 2 * kBN, wave, lane, ks2, vs2);
+    if (ST == 0 && two_ahead) issue_tile(a, b, g, k0 + 2 * kBN, wave, lane, ks2, vs2);
     if (kt + 1 <= kt_hi) {
       // This lane's loads of tile kt+1 were issued one step ago; tile kt+2's may still be
-      // in flight.  Cache stores also count, so after any, wait for all.  Every lane waits
-      // for its own loads before the barrier: other waves read them.
-      if (two_ahead && !stored) wait_vmcnt<kKLoads + kVLoads>(); else wait_vmcnt<0>();
-      finish_tile<LT>(a, b, g, k0 + kBN, q0, wave, lane, ks1, vs1, s_inv, stored);
+      // in flight.  Every lane waits for its own loads before the barrier: other waves
+      // read them.
+      if (two_ahead) wait_vmcnt<kKLoads + kVLoads>(); else wait_vmcnt<0>();
     }
     barrier_lds();
     __builtin_amdgcn_sched_barrier(0);   // keep the unrolled steps apart (register pressure)
@@ -435,11 +413,20 @@ void prefill_kernel(PrefillArgs a) {
 
 hipError_t launch_prefill(int layer_type, const PrefillArgs& a, hipStream_t stream) {
   const int blocks = a.nqb * a.batch * kKvHeads;
-  if (layer_type == kSliding)
+  const size_t chunks = (size_t)a.batch * a.seq_len * kKvHeads * 32;
+  const dim3 rope_grid((unsigned)((chunks + 255) / 256));
+  if (layer_type == kSliding) {
+    hipLaunchKernelGGL(prefill_rope_kernel<kSliding>, rope_grid, dim3(256), 0, stream, a);
     hipLaunchKernelGGL(prefill_kernel<kSliding>, dim3(blocks), dim3(kThreads), 0, stream, a);
-  else
+  } else {
+    hipLaunchKernelGGL(prefill_rope_kernel<kFull>, rope_grid, dim3(256), 0, stream, a);
     hipLaunchKernelGGL(prefill_kernel<kFull>, dim3(blocks), dim3(kThreads), 0, stream, a);
+  }
   return hipGetLastError();
+}
+
+size_t prefill_workspace_bytes(int batch, int seq_len) {
+  return (size_t)batch * seq_len * kKvHeads * kHeadDim * sizeof(uint16_t);
 }
 
 int prefill_block_rows() { return kBM; }

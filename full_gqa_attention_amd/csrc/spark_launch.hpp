@@ -11,6 +11,7 @@ struct PrefillArgs {
   const uint16_t* q;      // [B, S, 16, 256]
   const uint16_t* k;      // [B, S, 4, 256]
   const uint16_t* v;      // [B, S, 4, 256]
+  uint16_t* k_rot;        // [B, S, 4, 256] workspace: K after RoPE
   const uint16_t* gate;   // [B, S, 16]
   uint16_t* out;          // [B, S, 16, 256]
   uint16_t* cache_k;      // [B, cap, 4, 256] or null
@@ -54,6 +55,7 @@ hipError_t launch_append(int layer_type, const AppendArgs& a, hipStream_t stream
 hipError_t launch_decode(int layer_type, const DecodeArgs& a, hipStream_t stream);
 
 int prefill_block_rows();
+size_t prefill_workspace_bytes(int batch, int seq_len);
 
 // Decode planning, shared by the workspace query and the decode call.
 // Workspace regions are byte offsets from its start, each 256-byte aligned.

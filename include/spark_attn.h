@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define SPARK_ATTN_ABI_VERSION 2
+#define SPARK_ATTN_ABI_VERSION 3
 
 enum { SPARK_Q_HEADS = 16, SPARK_KV_HEADS = 4, SPARK_HEAD_DIM = 256, SPARK_WINDOW = 512 };
 
@@ -57,7 +57,7 @@ typedef enum spark_status {
   SPARK_OK = 0,
   SPARK_ERR_INVALID_ARG = 1, /* null pointer, bad enum, size out of range, misaligned */
   SPARK_ERR_UNSUPPORTED = 2, /* a valid request this build does not implement        */
-  SPARK_ERR_WORKSPACE = 3,   /* decode workspace smaller than required               */
+  SPARK_ERR_WORKSPACE = 3,   /* workspace smaller than required                      */
   SPARK_ERR_HIP = 4          /* the HIP runtime reported a launch failure            */
 } spark_status;
 
@@ -79,24 +79,35 @@ typedef struct spark_kv_cache {
 } spark_kv_cache;
 
 /*
+ * Bytes of device workspace spark_attn_prefill needs: the rotated keys,
+ * bf16 [batch, seq_len, 4, 256].  Returns 0 for sizes spark_attn_prefill would reject.
+ */
+size_t spark_attn_prefill_workspace_bytes(int32_t layer_type, int32_t batch, int32_t seq_len);
+
+/*
  * Prefill: attention of `seq_len` new tokens per sequence over themselves, one layer.
  *   q            bf16 [batch, seq_len, 16, 256], before RoPE
  *   k, v         bf16 [batch, seq_len, 4, 256], k before RoPE
  *   gate_logits  bf16 [batch, seq_len, 16]
- *   out          bf16 [batch, seq_len, 16, 256] (written)
  *   cache        optional (NULL = none): receives the rotated keys and the values of
  *                positions 0..seq_len-1 (SLIDING: only the last 512 of them, in their
  *                ring slots).  cache->batch must equal batch; FULL needs
  *                capacity >= seq_len.
- *   start_pos    position of the first token; this build supports 0 only
- *                (SPARK_ERR_UNSUPPORTED otherwise).
+ *   workspace    device scratch of at least spark_attn_prefill_workspace_bytes(...)
+ *                bytes, 256-byte aligned, used only during the call (calls sharing one
+ *                workspace must be ordered on a stream); SPARK_ERR_WORKSPACE if smaller
+ *   out          bf16 [batch, seq_len, 16, 256] (written)
+ *   start_pos    position of the first token; only 0 is supported (SPARK_ERR_UNSUPPORTED
+ *                otherwise).
  * Token t of a sequence sits at position start_pos + t.  1 <= seq_len <= 2^20,
- * 1 <= batch <= 65535.
+ * 1 <= batch <= 65535, batch * seq_len < 2^32.  Two launches: RoPE of K into the
+ * workspace (and the cache writes), then the attention with the sigmoid head gate.
  */
 spark_status spark_attn_prefill(int32_t layer_type, int32_t batch, int32_t seq_len,
                                 int32_t start_pos, const void* q, const void* k,
                                 const void* v, const void* gate_logits,
-                                const spark_kv_cache* cache, void* out, void* stream);
+                                const spark_kv_cache* cache, void* workspace,
+                                size_t workspace_bytes, void* out, void* stream);
 
 /*
  * Append `n_new` tokens per sequence to a layer's cache.

@@ -30,9 +30,9 @@ def test_exports_every_declared_function():
 
 
 def test_version_and_status_strings():
-    assert fga.abi_version() == 2
+    assert fga.abi_version() == 3
     assert fga.status_string(0) == "ok"
-    assert fga.status_string(3) == "decode workspace too small"
+    assert fga.status_string(3) == "workspace too small"
     assert fga.status_string(99) == "unknown status"
 
 
@@ -41,10 +41,11 @@ def _cache(k=FAKE, v=FAKE, batch=1, cap=512):
 
 
 def prefill(**kw):
-    a = dict(lt=1, B=1, S=16, start=0, q=FAKE, k=FAKE, v=FAKE, g=FAKE, cache=None, out=FAKE)
+    a = dict(lt=1, B=1, S=16, start=0, q=FAKE, k=FAKE, v=FAKE, g=FAKE, cache=None, ws=FAKE,
+             ws_bytes=1 << 30, out=FAKE)
     a.update(kw)
     return lib.spark_attn_prefill(a["lt"], a["B"], a["S"], a["start"], a["q"], a["k"], a["v"], a["g"],
-                                  a["cache"], a["out"], None)
+                                  a["cache"], a["ws"], a["ws_bytes"], a["out"], None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -53,9 +54,19 @@ def prefill(**kw):
     (dict(start=5), 2),
     (dict(lt=0, cache=_cache(cap=511)), 1), (dict(lt=1, cache=_cache(cap=15)), 1),
     (dict(cache=_cache(batch=2)), 1), (dict(cache=_cache(k=None)), 1),
+    (dict(ws=None), 1), (dict(ws=MISALIGNED), 1),
+    (dict(ws_bytes=16 * 4 * 256 * 2 - 1), 3),
+    (dict(B=65535, S=1 << 20), 1),            # batch * seq_len >= 2^32
 ])
 def test_prefill_rejects(kw, status):
     assert prefill(**kw) == status
+
+
+def test_prefill_workspace_planning():
+    ws = fga.prefill_workspace_bytes
+    assert ws(1, 1, 16) == 16 * 4 * 256 * 2            # rotated keys, bf16 [B, S, 4, 256]
+    assert ws(0, 3, 1000) == 3 * 1000 * 4 * 256 * 2
+    assert ws(2, 1, 16) == 0 and ws(1, 0, 16) == 0 and ws(1, 1, (1 << 20) + 1) == 0
 
 
 def test_append_rejects():
