@@ -58,6 +58,33 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
+// Maximum of a lane's 16 scores, with v_max3_f32 directly (no NaN occurs: masked scores
+// are -inf): fmaxf would first canonicalize every input.
+__device__ __forceinline__ float max16(const f32x16& x) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3\n\t"
+      "v_max3_f32 %0, %0, %4, %5\n\t"
+      "v_max3_f32 %0, %0, %6, %7\n\t"
+      "v_max3_f32 %0, %0, %8, %9\n\t"
+      "v_max3_f32 %0, %0, %10, %11\n\t"
+      "v_max3_f32 %0, %0, %12, %13\n\t"
+      "v_max3_f32 %0, %0, %14, %15\n\t"
+      "v_max_f32 %0, %0, %16"
+      : "=&v"(r)
+      : "v"(x[0]), "v"(x[1]), "v"(x[2]), "v"(x[3]), "v"(x[4]), "v"(x[5]), "v"(x[6]), "v"(x[7]),
+        "v"(x[8]), "v"(x[9]), "v"(x[10]), "v"(x[11]), "v"(x[12]), "v"(x[13]), "v"(x[14]), "v"(x[15]));
+  return r;
+}
+
+// max(x, x of lane l ^ 32): v_permlane32_swap hands every lane the values of lanes l % 32
+// and 32 + l % 32, i.e. its own and its partner's.
+__device__ __forceinline__ float max_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  float m;
+  asm("v_max_f32 %0, %1, %2" : "=v"(m) : "v"(__uint_as_float(r[0])), "v"(__uint_as_float(r[1])));
+  return m;
+}
+
 // Workgroup barrier that only waits for this wave's LDS operations.  __syncthreads()
 // would also wait for every outstanding global load, including the tile prefetched two
 // steps ahead; the loads a step depends on are waited for explicitly instead.
@@ -73,6 +100,23 @@ constexpr int kVLoads = 16 / kWaves;              // V-tile load instructions pe
 // keys.  Instruction n of K brings chunks 2n, 2n+1 of all 32 keys; instruction n of V rows
 // 2n, 2n+1 with chunk positions swizzled by 4 * (row % 4).  Rows past the end load row
 // S-1 (masked later).
+__device__ __forceinline__ void issue_one(const PrefillArgs& a, int b, int g, int k0, int wave,
+                                          int lane, uint8_t* ks, uint8_t* vs, int i) {
+  const int S = a.seq_len;
+  const size_t seq_row0 = (size_t)b * S;
+  if (i < kKLoads) {
+    const int pk = min(k0 + (lane & 31), S - 1);
+    const int n = kKLoads * wave + i;
+    const int chunk = 2 * n + (lane >> 5);
+    dma16(a.k_rot + ((seq_row0 + pk) * kKvHeads + g) * kHeadDim + 8 * chunk, ks + n * 1024);
+  } else {
+    const int n = kVLoads * wave + (i - kKLoads);
+    const int r = 2 * n + (lane >> 5);
+    const int chunk = (lane & 31) ^ (4 * (r & 3));
+    const int p = min(k0 + r, S - 1);
+    dma16(a.v + ((seq_row0 + p) * kKvHeads + g) * kHeadDim + 8 * chunk, vs + n * 1024);
+  }
+}
 __device__ __forceinline__ void issue_tile(const PrefillArgs& a, int b, int g, int k0, int wave,
                                            int lane, uint8_t* ks, uint8_t* vs) {
   const int S = a.seq_len;
@@ -292,8 +336,8 @@ void prefill_kernel(PrefillArgs a) {
     const bool two_ahead = kt + 2 <= kt_hi;
     // The compiler cannot follow per-stage loads across the loop back edge, so the first
     // LDS read of step 0 waits for every load in flight; step 0 therefore starts its
-    // prefetch after its MFMAs, the other steps before theirs.
-    if (ST != 0 && two_ahead) issue_tile(a, b, g, k0 + 2 * kBN, wave, lane, ks2, vs2);
+    // prefetch after its MFMAs, the other steps during their QK MFMAs (issuing a tile's
+    // loads back to back stalls every wave of the CU on the texture unit's queue).
 
     // Which row blocks see any key of this tile (wave-uniform).
     bool any[kRowBlocks], edge[kRowBlocks], any_rb = false;
@@ -313,6 +357,7 @@ void prefill_kernel(PrefillArgs a) {
         const bf16x8 ka = as_bf16x8(*reinterpret_cast<const u32x4*>(ks + (32 * (2 * s + half) + r32) * 16));
 #pragma unroll
         for (int rb = 0; rb < kRowBlocks; ++rb) sacc[rb] = mfma_32x32x16(ka, qf[rb][s], sacc[rb]);
+        if (ST != 0 && two_ahead && (s & 3) == 1) issue_one(a, b, g, k0 + 2 * kBN, wave, lane, ks2, vs2, s >> 2);
       }
       bf16x8 pf[kRowBlocks][2];
 #pragma unroll
@@ -326,10 +371,8 @@ void prefill_kernel(PrefillArgs a) {
             sacc[rb][v] = vis ? sacc[rb][v] : -INFINITY;
           }
         }
-        float mt = fmaxf(sacc[rb][0], sacc[rb][1]);
-#pragma unroll
-        for (int v = 2; v < 16; ++v) mt = fmaxf(mt, sacc[rb][v]);
-        mt = fmaxf(mt, __shfl_xor(mt, 32));
+        const float mt = max_halves(max16(sacc[rb]));
+        float l_pair[kRowBlocks][2] = {};   // two independent row-sum chains
         if (__any(mt > m_run[rb] + kRescaleThreshold)) {
           const float m_new = fmaxf(m_run[rb], mt);
           const float alpha = __builtin_amdgcn_exp2f(m_run[rb] - m_new);
@@ -347,11 +390,12 @@ void prefill_kernel(PrefillArgs a) {
             // pk: hipcc (ROCm 7.2) folds a bf16x2 bit-cast of pk[w] to pk[0] for every w.
             const bf16x2 p2 = {(__bf16)__builtin_amdgcn_exp2f(sacc[rb][8 * tt + 2 * w] - m_run[rb]),
                                (__bf16)__builtin_amdgcn_exp2f(sacc[rb][8 * tt + 2 * w + 1] - m_run[rb])};
-            l_part[rb] = __builtin_amdgcn_fdot2_f32_bf16(p2, ones, l_part[rb], false);
+            l_pair[rb][w & 1] = __builtin_amdgcn_fdot2_f32_bf16(p2, ones, l_pair[rb][w & 1], false);
             pk[w] = __builtin_bit_cast(uint32_t, p2);
           }
           pf[rb][tt] = as_bf16x8(pk);
         }
+        l_part[rb] += l_pair[rb][0] + l_pair[rb][1];
       }
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
@@ -366,7 +410,9 @@ void prefill_kernel(PrefillArgs a) {
         }
       }
     }
-    if (ST == 0 && two_ahead) issue_tile(a, b, g, k0 + 2 * kBN, wave, lane, ks2, vs2);
+    // Step 0 issues its prefetch after the MFMAs; the others issue it one instruction every
+    // four QK MFMAs, or here when this wave's rows see no key of the tile.
+    if (two_ahead && (ST == 0 || !any_rb)) issue_tile(a, b, g, k0 + 2 * kBN, wave, lane, ks2, vs2);
     if (kt + 1 <= kt_hi) {
       // This lane's loads of tile kt+1 were issued one step ago; tile kt+2's may still be
       // in flight.  Every lane waits for its own loads before the barrier: other waves
