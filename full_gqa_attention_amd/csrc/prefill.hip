@@ -58,31 +58,26 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
-// Maximum of a lane's 16 scores, with v_max3_f32 directly (no NaN occurs: masked scores
-// are -inf): fmaxf would first canonicalize every input.
+// Maximum of a lane's 16 scores, in code the compiler sees: the scores come straight from
+// an MFMA, and the compiler inserts the wait states a VALU read of an MFMA result needs
+// only before instructions it can see (an inline-asm v_max3_f32 chain here read the
+// accumulator while the MFMA was still writing it, on the path that skips the masking).
 __device__ __forceinline__ float max16(const f32x16& x) {
-  float r;
-  asm("v_max3_f32 %0, %1, %2, %3\n\t"
-      "v_max3_f32 %0, %0, %4, %5\n\t"
-      "v_max3_f32 %0, %0, %6, %7\n\t"
-      "v_max3_f32 %0, %0, %8, %9\n\t"
-      "v_max3_f32 %0, %0, %10, %11\n\t"
-      "v_max3_f32 %0, %0, %12, %13\n\t"
-      "v_max3_f32 %0, %0, %14, %15\n\t"
-      "v_max_f32 %0, %0, %16"
-      : "=&v"(r)
-      : "v"(x[0]), "v"(x[1]), "v"(x[2]), "v"(x[3]), "v"(x[4]), "v"(x[5]), "v"(x[6]), "v"(x[7]),
-        "v"(x[8]), "v"(x[9]), "v"(x[10]), "v"(x[11]), "v"(x[12]), "v"(x[13]), "v"(x[14]), "v"(x[15]));
-  return r;
+  float a = __builtin_fmaxf(__builtin_fmaxf(x[0], x[1]), x[2]);
+  float b = __builtin_fmaxf(__builtin_fmaxf(x[3], x[4]), x[5]);
+  float c = __builtin_fmaxf(__builtin_fmaxf(x[6], x[7]), x[8]);
+  float d = __builtin_fmaxf(__builtin_fmaxf(x[9], x[10]), x[11]);
+  float e = __builtin_fmaxf(__builtin_fmaxf(x[12], x[13]), x[14]);
+  a = __builtin_fmaxf(__builtin_fmaxf(a, b), c);
+  d = __builtin_fmaxf(__builtin_fmaxf(d, e), x[15]);
+  return __builtin_fmaxf(a, d);
 }
 
 // max(x, x of lane l ^ 32): v_permlane32_swap hands every lane the values of lanes l % 32
 // and 32 + l % 32, i.e. its own and its partner's.
 __device__ __forceinline__ float max_halves(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  float m;
-  asm("v_max_f32 %0, %1, %2" : "=v"(m) : "v"(__uint_as_float(r[0])), "v"(__uint_as_float(r[1])));
-  return m;
+  return __builtin_fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
 // Workgroup barrier that only waits for this wave's LDS operations.  __syncthreads()

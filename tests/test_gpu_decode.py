@@ -185,6 +185,21 @@ def test_prefill_then_decode_consistency(fga, lt):
     assert_parity(f64_of(out), want, f"prefill->append->decode lt={lt}")
 
 
+def test_decode_is_deterministic(fga):
+    """Repeated decode calls on the same cache give bit-identical outputs."""
+    import torch
+    lens = np.array([3000, 1500, 33, 4000, 512, 9000], np.int32)
+    B, cap = len(lens), int(lens.max())
+    d = synth.decode_inputs(5151, B, cap, fill_lens=lens)
+    cache = fga.KVCache(oracle.FULL, B, cap, k=to_dev(d["cache_k"]), v=to_dev(d["cache_v"]))
+    q, g, L = to_dev(d["q"]), to_dev(d["gate"]), i32_dev(lens)
+    ref = fga.decode(oracle.FULL, q, g, cache, L, cap).view(torch.int16).clone()
+    for rep in range(8):
+        out = fga.decode(oracle.FULL, q, g, cache, L, cap).view(torch.int16)
+        ndiff = int((out != ref).sum())
+        assert ndiff == 0, f"call {rep + 1}: {ndiff} output elements differ from the first call"
+
+
 def test_decode_rejects_small_workspace(fga):
     import torch
     cache = fga.KVCache(oracle.FULL, 1, 64)

@@ -97,6 +97,22 @@ def test_prefill_writes_cache(fga, lt, S):
     assert_parity(f64_of(out), want, f"prefill+cache lt={lt} S={S}")
 
 
+@pytest.mark.parametrize("lt", [oracle.SLIDING, oracle.FULL], ids=["sliding", "full"])
+def test_prefill_is_deterministic(fga, lt):
+    """Repeated calls on the same inputs give bit-identical outputs (no race between the
+    waves of a workgroup or between an MFMA and the instructions that read its result)."""
+    import torch
+    S = 8192
+    inp = synth.prefill_inputs(4242 + lt, 1, S)
+    q, k, v, g = (to_dev(inp[n]) for n in ("q", "k", "v", "gate"))
+    ws = torch.empty(fga.prefill_workspace_bytes(lt, 1, S), dtype=torch.uint8, device="cuda")
+    ref = fga.prefill(lt, q, k, v, g, workspace=ws).view(torch.int16).clone()
+    for rep in range(8):
+        out = fga.prefill(lt, q, k, v, g, workspace=ws).view(torch.int16)
+        ndiff = int((out != ref).sum())
+        assert ndiff == 0, f"call {rep + 1}: {ndiff} output elements differ from the first call"
+
+
 def test_prefill_rejects_bad_arguments(fga):
     import torch
     q = torch.zeros(1, 8, 16, 256, dtype=torch.bfloat16, device="cuda")
