@@ -47,9 +47,20 @@ constexpr float kQScale = 0.0625f * 1.4426950408889634f;   // 1/sqrt(256) * log2
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
+// Direct global -> LDS load of 16 bytes per lane into the 1 KB block at lds_block (lane l
+// fills bytes 16l .. 16l+15).  Written as inline asm so that the compiler does not track
+// it: given the builtin, it cannot tell which ring stage a load fills and waits for every
+// load in flight before the first LDS read of some steps.  Every wait for these loads is
+// therefore explicit (wait_vmcnt before the barrier that publishes a tile).  The asm sets
+// M0, which nothing else in these kernels uses.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"   // M0 in the clobber list: see above
 __device__ __forceinline__ void dma16(const void* src, void* lds_block) {
-  __builtin_amdgcn_global_load_lds(src, lds_block, 16, 0, 0);
+  const uint32_t lds = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)lds_block;
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :: "v"(src), "s"(lds) : "memory", "m0");
 }
+#pragma clang diagnostic pop
 
 // vmcnt <= N, other counters untouched.
 template <int N>
@@ -253,9 +264,7 @@ template <int LT>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves / 4, kWaves / 4)))
 void prefill_kernel(PrefillArgs a) {
   using T = LayerTraits<LT>;
-  // One array per stage and operand: the loop below is unrolled by the stage count, so
-  // the compiler can tell that reads of one stage never alias the loads in flight into
-  // the others, and does not wait for those loads before reading.
+  // One array per stage and operand; the loop below is unrolled by the stage count.
   __shared__ __attribute__((aligned(1024))) uint8_t s_k0[kTileBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t s_v0[kTileBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t s_k1[kTileBytes];
@@ -294,9 +303,7 @@ void prefill_kernel(PrefillArgs a) {
 #pragma unroll
   for (int rb = 0; rb < kRowBlocks; ++rb) load_q<LT>(a, b, hq, q0 + 32 * (rb0 + rb) + r32, half, s_inv, qf[rb]);
 
-  // First tile: wait for this lane's loads, publish.  Waiting for the second tile too
-  // leaves no load in flight on entry to the loop, which lets the compiler keep exact
-  // track of the loads in flight per stage inside it.
+  // First tiles: wait for this lane's loads (of both), publish.
   wait_vmcnt<0>();
   barrier_lds();
 
@@ -329,10 +336,9 @@ void prefill_kernel(PrefillArgs a) {
     uint8_t* const vs2 = ST == 0 ? s_v2 : ST == 1 ? s_v0 : s_v1;
     const int k0 = kt * kBN;
     const bool two_ahead = kt + 2 <= kt_hi;
-    // The compiler cannot follow per-stage loads across the loop back edge, so the first
-    // LDS read of step 0 waits for every load in flight; step 0 therefore starts its
-    // prefetch after its MFMAs, the other steps during their QK MFMAs (issuing a tile's
-    // loads back to back stalls every wave of the CU on the texture unit's queue).
+    // Steps 1 and 2 issue tile kt+2 one load every four QK MFMAs (issuing a tile's loads
+    // back to back stalls every wave of the CU on the texture unit's queue); step 0
+    // issues it after its MFMAs, which measured slightly faster than interleaving there.
 
     // Which row blocks see any key of this tile (wave-uniform).
     bool any[kRowBlocks], edge[kRowBlocks], any_rb = false;
