@@ -97,6 +97,135 @@ def bench_decode(fga, synth, steps, warmup):
     return {"ms": ms, "bytes": kv_bytes + io_bytes, "gbs": gbs, "lens_sum": int(lens.sum())}
 
 
+def dev_normal(gen, shape):
+    """Seeded N(0,1) bf16 tensor drawn on the device (for the large timing-only inputs)."""
+    import torch
+    return torch.randn(shape, generator=gen, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+
+
+def time_each(fn, n, warmup, before=None):
+    """Median ms of ``n`` single calls, each bracketed by HIP events; ``before`` runs
+    (untimed) ahead of every call, e.g. to evict the caches."""
+    import statistics
+    import torch
+    for _ in range(warmup):
+        fn()
+    times = []
+    stream = torch.cuda.current_stream()
+    for _ in range(n):
+        if before is not None:
+            before()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+    return statistics.median(times)
+
+
+def sliding_pairs(S):
+    return sum(min(i + 1, 512) for i in range(S))
+
+
+def bench_configs(fga, synth):
+    """The other workloads of the hot path's scope table, each timed on its own:
+    sliding prefill S=1024; the 36-layer stack at S=32768; batched decode (full, cold
+    caches; sliding ring, warm and cold); long decode at 128K and 1M tokens."""
+    import numpy as np
+    import torch
+    out = {}
+    gen = torch.Generator(device="cuda")
+
+    # Config 1: one sliding layer, batch 1, S = 1024 (host-drawn inputs, as in the tests).
+    S = 1024
+    inp = synth.prefill_inputs(synth.CONFIG_SEED[1], 1, S)
+    q, k, v, g = (to_dev(inp[n]) for n in ("q", "k", "v", "gate"))
+    o = torch.empty_like(q)
+    ws = torch.empty(fga.prefill_workspace_bytes(fga.SLIDING, 1, S), dtype=torch.uint8, device="cuda")
+    ms = time_launches(lambda: fga.prefill(fga.SLIDING, q, k, v, g, out=o, workspace=ws), 200, 50)
+    tf = 16384 * sliding_pairs(S) / (ms * 1e-3) / 1e12
+    out["sliding_prefill_s1024"] = {"ms": ms, "tflops": tf, "frac_mfma": tf / PEAK_BF16_TFLOPS,
+                                    "tokens_per_s": S / (ms * 1e-3)}
+    log(f"config 1 sliding prefill S=1024: {ms * 1e3:.1f} us  {tf:.0f} TFLOP/s")
+    del q, k, v, g, o, ws
+
+    # Config 4: 36-layer stack, batch 1, S = 32768, independent inputs per layer (drawn on
+    # the device: 24 GB of N(0,1) bf16); layer l is full iff l % 4 == 3.
+    S = 32768
+    gen.manual_seed(synth.CONFIG_SEED[4])
+    layers = []
+    for layer in range(36):
+        layers.append(((fga.FULL if layer % 4 == 3 else fga.SLIDING),
+                       dev_normal(gen, (1, S, 16, 256)), dev_normal(gen, (1, S, 4, 256)),
+                       dev_normal(gen, (1, S, 4, 256)), dev_normal(gen, (1, S, 16)),
+                       torch.empty(1, S, 16, 256, dtype=torch.bfloat16, device="cuda")))
+    ws = torch.empty(fga.prefill_workspace_bytes(fga.FULL, 1, S), dtype=torch.uint8, device="cuda")
+
+    def stack():
+        for lt, q, k, v, g, o in layers:
+            fga.prefill(lt, q, k, v, g, out=o, workspace=ws)
+
+    ms = time_launches(stack, 5, 2)
+    flops = 9 * 16384 * (S * (S + 1) // 2) + 27 * 16384 * sliding_pairs(S)
+    tf = flops / (ms * 1e-3) / 1e12
+    out["stack36_prefill_s32768"] = {"ms": ms, "tflops": tf, "frac_mfma": tf / PEAK_BF16_TFLOPS,
+                                     "tokens_per_s": S / (ms * 1e-3), "tflop": flops / 1e12}
+    log(f"config 4 36-layer stack S=32768: {ms:.2f} ms  {tf:.0f} TFLOP/s")
+    del layers, ws
+    torch.cuda.empty_cache()
+
+    # A 1 GiB buffer copied before each cold call evicts the 256 MB MALL and the L2s.
+    flush_a = torch.empty(1 << 29, dtype=torch.bfloat16, device="cuda")
+    flush_b = torch.empty_like(flush_a)
+    flush = lambda: flush_b.copy_(flush_a)
+
+    def decode_case(lt, B, lens, cap, seed, cold):
+        lens = np.asarray(lens, dtype=np.int32)
+        gen.manual_seed(seed)
+        qd = dev_normal(gen, (B, 16, 256))
+        gd = dev_normal(gen, (B, 16))
+        cache = fga.KVCache(lt, B, cap, k=dev_normal(gen, (B, cap, 4, 256)),
+                            v=dev_normal(gen, (B, cap, 4, 256)))
+        sl = torch.as_tensor(lens).cuda()
+        maxlen = int(lens.max())
+        wsd = torch.empty(fga.decode_workspace_bytes(lt, B, maxlen), dtype=torch.uint8, device="cuda")
+        od = torch.empty_like(qd)
+        call = lambda: fga.decode(lt, qd, gd, cache, sl, maxlen, out=od, workspace=wsd)
+        ms = time_each(call, 30, 5, flush if cold else None)
+        vis = np.minimum(lens, 512) if lt == fga.SLIDING else lens
+        nbytes = int(vis.astype(np.int64).sum()) * 4096 + B * (16 * 256 * 4 + 32)
+        return {"us": ms * 1e3, "gbs": nbytes / (ms * 1e-3) / 1e9,
+                "frac_hbm": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, "bytes": nbytes,
+                "cache": "cold" if cold else "warm"}
+
+    # Config 3: batch 64, lengths uniform in [1024, 32768].
+    seed = synth.CONFIG_SEED[3]
+    lens = synth.decode_seq_lens(seed, 64, 1024, 32768)
+    r = decode_case(fga.FULL, 64, lens, 32768, seed, cold=True)
+    out["decode_b64_full_cold"] = r
+    log(f"config 3 decode full, cold: {r['us']:.0f} us  {r['gbs']:.0f} GB/s")
+    torch.cuda.empty_cache()
+    for cold in (False, True):
+        r = decode_case(fga.SLIDING, 64, lens, 512, seed + 1, cold=cold)
+        out[f"decode_b64_sliding_{r['cache']}"] = r
+        log(f"config 3 decode sliding ring, {r['cache']}: {r['us']:.1f} us  {r['gbs']:.0f} GB/s")
+
+    # Config 5: long decode, full layer (cache capacity = L) and the sliding ring.
+    for B, L in ((4, 131072), (1, 1 << 20)):
+        r = decode_case(fga.FULL, B, [L] * B, L, synth.CONFIG_SEED[5] + B, cold=True)
+        out[f"decode_full_b{B}_l{L}_cold"] = r
+        log(f"config 5 decode full B={B} L={L}, cold: {r['us']:.0f} us  {r['gbs']:.0f} GB/s")
+        torch.cuda.empty_cache()
+        r = decode_case(fga.SLIDING, B, [L] * B, 512, synth.CONFIG_SEED[5] + 10 + B, cold=True)
+        out[f"decode_sliding_b{B}_l{L}_cold"] = r
+        log(f"config 5 decode sliding B={B} L={L}, cold: {r['us']:.1f} us")
+    del flush_a, flush_b
+    torch.cuda.empty_cache()
+    return out
+
+
 def copy_calibration():
     """Device-to-device copy of 4 GiB: the plain copy of known size that scales the HBM
     traffic counters (run under rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE)."""
@@ -166,6 +295,8 @@ def main():
     ap.add_argument("--skip-decode", action="store_true")
     ap.add_argument("--skip-prefill", action="store_true")
     ap.add_argument("--skip-cpu-baseline", action="store_true")
+    ap.add_argument("--skip-configs", action="store_true",
+                    help="skip the other workloads (sliding prefill, 36-layer stack, decode variants)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run the 4 GiB device copy used to scale traffic counters")
     args = ap.parse_args()
@@ -211,6 +342,9 @@ def main():
                          "frac": d["gbs"] / PEAK_HBM_GBS, "traffic": measured_traffic("decode_full")},
         }
         log(f"decode {d['ms']:.3f} ms  {d['gbs']:.0f} GB/s")
+    if not args.skip_configs:
+        log("other workloads ...")
+        result["configs"] = bench_configs(fga, synth)
     if not args.skip_cpu_baseline:
         log("cpu baseline (oracle) ...")
         result["cpu_baseline"] = cpu_baseline(synth)
