@@ -176,10 +176,11 @@ def bench_configs(fga, synth):
     del layers, ws
     torch.cuda.empty_cache()
 
-    # A 1 GiB buffer copied before each cold call evicts the 256 MB MALL and the L2s.
-    flush_a = torch.empty(1 << 29, dtype=torch.bfloat16, device="cuda")
-    flush_b = torch.empty_like(flush_a)
-    flush = lambda: flush_b.copy_(flush_a)
+    # Reading a 1 GiB buffer before each cold call evicts the 256 MB MALL and the L2s.  (A
+    # copy would also evict them, but leaves dirty lines whose write-back then competes
+    # with the timed call.)
+    flush_a = torch.ones(1 << 29, dtype=torch.bfloat16, device="cuda")
+    flush = lambda: flush_a.sum()
 
     def decode_case(lt, B, lens, cap, seed, cold):
         lens = np.asarray(lens, dtype=np.int32)
@@ -221,7 +222,7 @@ def bench_configs(fga, synth):
         r = decode_case(fga.SLIDING, B, [L] * B, 512, synth.CONFIG_SEED[5] + 10 + B, cold=True)
         out[f"decode_sliding_b{B}_l{L}_cold"] = r
         log(f"config 5 decode sliding B={B} L={L}, cold: {r['us']:.1f} us")
-    del flush_a, flush_b
+    del flush_a
     torch.cuda.empty_cache()
     return out
 

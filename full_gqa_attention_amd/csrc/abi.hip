@@ -146,9 +146,7 @@ spark_status spark_attn_decode(int32_t layer_type, int32_t batch, const void* q,
   a.cache_k = static_cast<const uint16_t*>(cache->k);
   a.cache_v = static_cast<const uint16_t*>(cache->v);
   a.seq_lens = seq_lens;
-  a.ws_cum = reinterpret_cast<int32_t*>(ws + plan.cum_offset);
   a.ws_range = reinterpret_cast<int2*>(ws + plan.range_offset);
-  a.ws_first = reinterpret_cast<int32_t*>(ws + plan.first_offset);
   a.ws_o = reinterpret_cast<float*>(ws + plan.o_offset);
   a.ws_ml = reinterpret_cast<float*>(ws + plan.ml_offset);
   a.out = static_cast<uint16_t*>(out);

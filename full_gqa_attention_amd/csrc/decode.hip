@@ -4,11 +4,13 @@
 // hotelren.com/news/5475707, section 二: each generated token re-reads its state), so
 // every cache byte is read exactly once and the whole batch's reads are spread evenly
 // over the workgroups:
-//   * plan: sequence b owns c_b = ceil(n_b / 32) chunks of 32 visible keys; the chunks of
-//     all sequences are numbered back to back (prefix sums cum[b]) and partition w of P
-//     takes chunks [floor(wC/P), floor((w+1)C/P)).  A one-workgroup kernel computes cum
-//     and the first sequence of each partition on the device, so no host sync is needed
-//     and uneven context lengths still give every workgroup the same amount of traffic.
+//   * partition: sequence b owns c_b = ceil(n_b / 32) chunks of 32 visible keys; the chunks
+//     of all sequences are numbered back to back and partition w of P takes chunks
+//     [floor(wC/P), floor((w+1)C/P)).  Every workgroup computes the prefix sums of the c_b
+//     itself (a scan over the batch in LDS) and finds its first sequence, so the plan costs
+//     no launch and no host sync, and uneven context lengths still give every workgroup
+//     the same amount of traffic.  Workgroup 0 also records, for the merge, the range of
+//     partitions that touch each sequence.
 //   * split: workgroup w walks its chunks; each run of chunks inside one sequence is a
 //     segment with its own online softmax, written as a partial result (max, sum,
 //     unnormalised O per query head) to slot w + b, which is unique because both w and b
@@ -21,8 +23,7 @@
 //       - O += P V on the VALU in fp32: V rows are loaded fully coalesced (two 512-byte
 //         rows per instruction), each lane owns 8 dims of one key parity, P from LDS.
 //   * merge: per (sequence, query head), the partials of the partitions that touched the
-//     sequence (a range the plan records) are combined with log-sum-exp weights and the
-//     sigmoid head gate is applied.
+//     sequence are combined with log-sum-exp weights and the sigmoid head gate is applied.
 // Sliding layers read the 512-slot ring; full layers the contiguous cache.
 #include "spark_device.hpp"
 #include "spark_launch.hpp"
@@ -33,7 +34,6 @@ namespace {
 constexpr int kThreads = 256;   // 4 waves = 4 KV heads
 constexpr int kChunk = 32;      // keys per inner iteration and per partition unit
 constexpr int kSlot = kKvHeads * kHeadDim;   // bf16 per cache slot
-constexpr int kPlanThreads = 1024;
 
 template <int LT>
 __device__ __forceinline__ int visible_keys(int L, int cap) {
@@ -54,44 +54,6 @@ __device__ __forceinline__ int part_lo(int w, int C, int P) {
 // Partition holding chunk x: the largest w with floor(w C / P) <= x.
 __device__ __forceinline__ int part_of(int x, int C, int P) {
   return (int)((((long long)(x + 1) * P) + C - 1) / C) - 1;
-}
-
-template <int LT>
-__global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(DecodeArgs a) {
-  __shared__ int s_scan[kPlanThreads];
-  const int t = threadIdx.x;
-  const int per = (a.batch + kPlanThreads - 1) / kPlanThreads;
-  const int b0 = min(t * per, a.batch);
-  const int b1 = min(b0 + per, a.batch);
-  int own = 0;
-  for (int b = b0; b < b1; ++b) own += chunks_of<LT>(a.seq_lens[b], a.cache_cap);
-  s_scan[t] = own;
-  __syncthreads();
-  for (int off = 1; off < kPlanThreads; off <<= 1) {
-    const int add = t >= off ? s_scan[t - off] : 0;
-    __syncthreads();
-    s_scan[t] += add;
-    __syncthreads();
-  }
-  const int C = s_scan[kPlanThreads - 1];
-  const int P = min(a.nparts, C);            // so that no partition is empty
-  int run = s_scan[t] - own;
-  for (int b = b0; b < b1; ++b) {
-    const int c = chunks_of<LT>(a.seq_lens[b], a.cache_cap);
-    a.ws_cum[b] = run;
-    if (c > 0) {
-      // Partitions whose first chunk falls in [run, run + c) start in sequence b.
-      const int w0 = (int)(((long long)run * P + C - 1) / C);
-      const int w1 = (int)(((long long)(run + c) * P + C - 1) / C);
-      for (int w = w0; w < w1; ++w) a.ws_first[w] = b;
-      // Partitions touching b: those holding its first and its last chunk, and all between.
-      a.ws_range[b] = int2{part_of(run, C, P), part_of(run + c - 1, C, P)};
-    } else {
-      a.ws_range[b] = int2{0, -1};
-    }
-    run += c;
-  }
-  if (t == kPlanThreads - 1) a.ws_cum[a.batch] = C;
 }
 
 // Online-softmax attention of the 4 query heads of KV head g of sequence b over keys
@@ -252,31 +214,65 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) float s_p[kKvHeads][kChunk][4];
   __shared__ __attribute__((aligned(16))) float s_alpha[kKvHeads][4];
 
+  __shared__ int s_scan[kThreads];
+
+  // Chunk counts of the batch: thread t owns sequences [t per, t per + per); inclusive
+  // prefix sums over the threads.
+  const int tid = threadIdx.x;
+  const int per = (a.batch + kThreads - 1) / kThreads;
+  const int b0 = min(tid * per, a.batch);
+  const int b1 = min(b0 + per, a.batch);
+  int own = 0;
+  for (int b = b0; b < b1; ++b) own += chunks_of<LT>(a.seq_lens[b], a.cache_cap);
+  s_scan[tid] = own;
+  __syncthreads();
+  for (int off = 1; off < kThreads; off <<= 1) {
+    const int add = tid >= off ? s_scan[tid - off] : 0;
+    __syncthreads();
+    s_scan[tid] += add;
+    __syncthreads();
+  }
+  const int C = s_scan[kThreads - 1];
+  const int P = min(a.nparts, C);            // so that no partition is empty
   const int w = blockIdx.x;
-  const int C = a.ws_cum[a.batch];
-  const int P = min(a.nparts, C);            // as planned: every partition below P has chunks
+  if (w == 0) {
+    // Partitions touching each sequence: those holding its first and its last chunk, and
+    // all between (read by the merge).
+    int run = s_scan[tid] - own;
+    for (int b = b0; b < b1; ++b) {
+      const int c = chunks_of<LT>(a.seq_lens[b], a.cache_cap);
+      a.ws_range[b] = c > 0 ? int2{part_of(run, C, P), part_of(run + c - 1, C, P)} : int2{0, -1};
+      run += c;
+    }
+  }
   if (w >= P) return;                        // uniform over the workgroup
   const int lo = part_lo(w, C, P);
   const int hi = part_lo(w + 1, C, P);
 
-  const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int g = __builtin_amdgcn_readfirstlane(tid >> 6);
   if (tid < T::kRot / 2) s_inv[tid] = rope_inv_rev(tid, T::kRot, log2(T::kTheta));
   __syncthreads();
 
-  int b = a.ws_first[w];
-  int cb = a.ws_cum[b];
+  // The thread owning chunk lo is the first whose inclusive prefix exceeds lo; walk its
+  // sequences from there.  Each sequence with chunks in [lo, hi) is one segment.
+  int t0 = 0, t1 = kThreads - 1;
+  while (t0 < t1) {
+    const int mid = (t0 + t1) >> 1;
+    if (s_scan[mid] > lo) t1 = mid; else t0 = mid + 1;
+  }
+  int b = min(t0 * per, a.batch);
+  int cb = t0 > 0 ? s_scan[t0 - 1] : 0;      // chunks before sequence b
   for (;;) {
-    const int cn = a.ws_cum[b + 1];
-    if (cn > cb) {
-      const int L = a.seq_lens[b];
-      const int n = visible_keys<LT>(L, a.cache_cap);
+    const int L = a.seq_lens[b];
+    const int n = visible_keys<LT>(L, a.cache_cap);
+    const int cn = cb + (n + kChunk - 1) / kChunk;
+    if (cn > lo && cn > cb) {
       const int ks = (max(lo, cb) - cb) * kChunk;
       const int ke = min((min(hi, cn) - cb) * kChunk, n);
       attend_segment<LT>(a, b, L, ks, ke, w + b, g, lane, s_inv, s_p, s_alpha);
     }
-    if (cn >= hi) break;                     // then b + 1 < batch, since cum[batch] >= hi
+    if (cn >= hi || b + 1 >= a.batch) break;
     ++b;
     cb = cn;
   }
@@ -284,15 +280,21 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
 
 // One wave per (sequence, query head); lane l owns dims 4l..4l+3.  The partials are
 // merged in one online pass: running max, rescaled sum and rescaled output.
-__global__ __launch_bounds__(64) void decode_reduce_kernel(DecodeArgs a) {
+constexpr int kReduceWaves = 4;
+
+__global__ __launch_bounds__(64 * kReduceWaves) void decode_reduce_kernel(DecodeArgs a) {
+  __shared__ float s_ml[kReduceWaves][2];
+  __shared__ f32x4 s_o[kReduceWaves][64];
   const int b = blockIdx.x / kQHeads;
   const int h = blockIdx.x % kQHeads;
-  const int lane = threadIdx.x;
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
   const int2 r = a.ws_range[b];
+  // Wave v merges partitions r.x + v, r.x + v + 4, ... (lane: dims 4 lane .. 4 lane + 3).
   float m = -1e30f, l = 0.0f;
   f32x4 o = f32x4{0, 0, 0, 0};
 #pragma unroll 4
-  for (int w = r.x; w <= r.y; ++w) {
+  for (int w = r.x + wave; w <= r.y; w += kReduceWaves) {
     const size_t hs = (size_t)(w + b) * kQHeads + h;
     const float2 ml = *reinterpret_cast<const float2*>(a.ws_ml + hs * 2);
     const f32x4 ow = *reinterpret_cast<const f32x4*>(a.ws_o + hs * kHeadDim + 4 * lane);
@@ -303,11 +305,26 @@ __global__ __launch_bounds__(64) void decode_reduce_kernel(DecodeArgs a) {
     o = o * sa + ow * sb;
     m = mn;
   }
+  if (lane == 0) { s_ml[wave][0] = m; s_ml[wave][1] = l; }
+  s_o[wave][lane] = o;
+  __syncthreads();
+  if (wave != 0) return;
+  float mt = s_ml[0][0];
+#pragma unroll
+  for (int v = 1; v < kReduceWaves; ++v) mt = fmaxf(mt, s_ml[v][0]);
+  float lt = 0.0f;
+  f32x4 ot = f32x4{0, 0, 0, 0};
+#pragma unroll
+  for (int v = 0; v < kReduceWaves; ++v) {
+    const float sv = __builtin_amdgcn_exp2f(s_ml[v][0] - mt);
+    lt += s_ml[v][1] * sv;
+    ot += s_o[v][lane] * sv;
+  }
   // No visible key (r empty): l = 0 and o = 0, written as zeros.
   const float gl = bf16_to_f32(a.gate[(size_t)b * kQHeads + h]);
-  const float sc = l > 0.0f ? sigmoidf_fast(gl) / l : 0.0f;
+  const float sc = lt > 0.0f ? sigmoidf_fast(gl) / lt : 0.0f;
   uint16_t* dst = a.out + ((size_t)b * kQHeads + h) * kHeadDim + 4 * lane;
-  *reinterpret_cast<u32x2*>(dst) = u32x2{pack_bf16x2(o[0] * sc, o[1] * sc), pack_bf16x2(o[2] * sc, o[3] * sc)};
+  *reinterpret_cast<u32x2*>(dst) = u32x2{pack_bf16x2(ot[0] * sc, ot[1] * sc), pack_bf16x2(ot[2] * sc, ot[3] * sc)};
 }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -337,10 +354,8 @@ DecodePlan plan_decode(int layer_type, int batch, int max_seq_len, int nparts) {
     if (P < 1) P = 1;
   }
   p.nparts = P;
-  p.cum_offset = 0;
-  p.range_offset = align256((size_t)(batch + 1) * sizeof(int32_t));
-  p.first_offset = p.range_offset + align256((size_t)batch * 2 * sizeof(int32_t));
-  p.o_offset = p.first_offset + align256((size_t)P * sizeof(int32_t));
+  p.range_offset = 0;
+  p.o_offset = align256((size_t)batch * 2 * sizeof(int32_t));
   const size_t slots = (size_t)P + batch;
   p.ml_offset = p.o_offset + align256(slots * kQHeads * kHeadDim * sizeof(float));
   p.total_bytes = p.ml_offset + slots * kQHeads * 2 * sizeof(float);
@@ -350,13 +365,11 @@ DecodePlan plan_decode(int layer_type, int batch, int max_seq_len, int nparts) {
 hipError_t launch_decode(int layer_type, const DecodeArgs& a, hipStream_t stream) {
   const dim3 grid_reduce(a.batch * kQHeads);
   if (layer_type == kSliding) {
-    hipLaunchKernelGGL(decode_plan_kernel<kSliding>, dim3(1), dim3(kPlanThreads), 0, stream, a);
     hipLaunchKernelGGL(decode_split_kernel<kSliding>, dim3(a.nparts), dim3(kThreads), 0, stream, a);
-    hipLaunchKernelGGL(decode_reduce_kernel, grid_reduce, dim3(64), 0, stream, a);
+    hipLaunchKernelGGL(decode_reduce_kernel, grid_reduce, dim3(64 * kReduceWaves), 0, stream, a);
   } else {
-    hipLaunchKernelGGL(decode_plan_kernel<kFull>, dim3(1), dim3(kPlanThreads), 0, stream, a);
     hipLaunchKernelGGL(decode_split_kernel<kFull>, dim3(a.nparts), dim3(kThreads), 0, stream, a);
-    hipLaunchKernelGGL(decode_reduce_kernel, grid_reduce, dim3(64), 0, stream, a);
+    hipLaunchKernelGGL(decode_reduce_kernel, grid_reduce, dim3(64 * kReduceWaves), 0, stream, a);
   }
   return hipGetLastError();
 }

@@ -39,9 +39,7 @@ struct DecodeArgs {
   const uint16_t* cache_k;
   const uint16_t* cache_v;
   const int32_t* seq_lens;
-  int32_t* ws_cum;        // [B + 1] prefix sums of the per-sequence 32-key chunk counts
   int2* ws_range;         // [B] first and last partition touching each sequence
-  int32_t* ws_first;      // [P] sequence holding the first chunk of each partition
   float* ws_o;            // [P + B, 16, 256] partial results, slot = partition + sequence
   float* ws_ml;           // [P + B, 16, 2] (max, sum) per partial
   uint16_t* out;          // [B, 16, 256]
@@ -61,9 +59,7 @@ size_t prefill_workspace_bytes(int batch, int seq_len);
 // Workspace regions are byte offsets from its start, each 256-byte aligned.
 struct DecodePlan {
   int nparts;
-  size_t cum_offset;
   size_t range_offset;
-  size_t first_offset;
   size_t o_offset;
   size_t ml_offset;
   size_t total_bytes;

@@ -126,7 +126,8 @@ spark_status spark_kv_append(int32_t layer_type, int32_t batch, int32_t n_new,
  * Bytes of device workspace spark_attn_decode needs for this shape and partition count
  * (num_parts = 0 lets the library choose, exactly as spark_attn_decode will).  The size
  * grows with batch and num_parts only: (num_parts + batch) partial results of 16 x 258
- * floats, plus the partition plan.  Returns 0 for arguments spark_attn_decode would reject.
+ * floats, plus each sequence's partition range.  Returns 0 for arguments
+ * spark_attn_decode would reject.
  */
 size_t spark_attn_decode_workspace_bytes(int32_t layer_type, int32_t batch,
                                          int32_t max_seq_len, int32_t num_parts);
@@ -147,9 +148,9 @@ size_t spark_attn_decode_workspace_bytes(int32_t layer_type, int32_t batch,
  *                workspace must be ordered on a stream)
  *   out          bf16 [batch, 16, 256] (written)
  * FULL layers read positions 0..L-1; SLIDING layers read positions max(0, L-512)..L-1
- * from the ring (attention over a set of keys does not depend on their order).  Three
- * launches: the partition plan (prefix sums of chunk counts, computed on the device),
- * attention with per-(partition, sequence) partial results, then a log-sum-exp merge
+ * from the ring (attention over a set of keys does not depend on their order).  Two
+ * launches: attention with per-(partition, sequence) partial results (each workgroup
+ * derives its share of the batch from seq_lens on the device), then a log-sum-exp merge
  * that also applies the gate.
  */
 spark_status spark_attn_decode(int32_t layer_type, int32_t batch, const void* q,

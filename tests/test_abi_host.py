@@ -79,13 +79,12 @@ def test_append_rejects():
 
 
 def _layout_bytes(batch, parts):
-    """The workspace layout: chunk prefix sums [batch + 1], partition range of each sequence
-    [batch, 2] and first sequence of each partition [parts] (int32), then (parts + batch)
-    partials of 16 x 256 floats and of 16 x 2 floats, each region 256-byte aligned."""
+    """The workspace layout: partition range of each sequence [batch, 2] (int32), then
+    (parts + batch) partials of 16 x 256 floats and of 16 x 2 floats, each region 256-byte
+    aligned."""
     up = lambda x: (x + 255) // 256 * 256
     slots = parts + batch
-    return (up(4 * (batch + 1)) + up(8 * batch) + up(4 * parts) + up(slots * 16 * 256 * 4)
-            + slots * 16 * 2 * 4)
+    return up(8 * batch) + up(slots * 16 * 256 * 4) + slots * 16 * 2 * 4
 
 
 def test_workspace_planning():

@@ -185,6 +185,23 @@ def test_prefill_then_decode_consistency(fga, lt):
     assert_parity(f64_of(out), want, f"prefill->append->decode lt={lt}")
 
 
+@pytest.mark.parametrize("num_parts", [0, 7, 4000])
+def test_decode_batch_beyond_plan_threads(fga, num_parts):
+    """A batch of 1500 sequences (more than the plan's 1024 threads, so each thread owns two)
+    with lengths 0..64, some empty: every partition must find its first sequence."""
+    B, cap = 1500, 64
+    lens = np.random.default_rng(77).integers(0, cap + 1, size=B).astype(np.int32)
+    lens[::97] = 0
+    d = synth.decode_inputs(6060, B, cap, fill_lens=lens)
+    note(f"decode B={B} parts={num_parts}")
+    got = _decode_dev(fga, oracle.FULL, d, d["cache_k"], d["cache_v"], lens, num_parts, max_len=cap)
+    live = lens > 0
+    want = oracle.decode(d["q"][live], d["gate"][live], d["cache_k"][live], d["cache_v"][live],
+                         lens[live], oracle.FULL)
+    assert_parity(got[live], want, f"decode B={B} parts={num_parts}")
+    assert np.all(got[~live] == 0.0)
+
+
 def test_decode_is_deterministic(fga):
     """Repeated decode calls on the same cache give bit-identical outputs."""
     import torch
