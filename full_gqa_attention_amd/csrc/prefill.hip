@@ -264,13 +264,14 @@ template <int LT>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves / 4, kWaves / 4)))
 void prefill_kernel(PrefillArgs a) {
   using T = LayerTraits<LT>;
-  // One array per stage and operand; the loop below is unrolled by the stage count.
-  __shared__ __attribute__((aligned(1024))) uint8_t s_k0[kTileBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t s_v0[kTileBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t s_k1[kTileBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t s_v1[kTileBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t s_k2[kTileBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t s_v2[kTileBytes];
+  // The ring: [stage][K, V]; the loop below is unrolled by the stage count.
+  __shared__ __attribute__((aligned(1024))) uint8_t s_ring[3][2][kTileBytes];
+  uint8_t* const s_k0 = &s_ring[0][0][0];
+  uint8_t* const s_v0 = &s_ring[0][1][0];
+  uint8_t* const s_k1 = &s_ring[1][0][0];
+  uint8_t* const s_v1 = &s_ring[1][1][0];
+  uint8_t* const s_k2 = &s_ring[2][0][0];
+  uint8_t* const s_v2 = &s_ring[2][1][0];
   __shared__ double s_inv[T::kRot / 2];
 
   const int tid = threadIdx.x;
@@ -434,22 +435,63 @@ void prefill_kernel(PrefillArgs a) {
   }
 
   // ---- epilogue: O / l * sigmoid(gate), bf16
+  if constexpr (T::kWindowed) {
+    static_assert(kRowBlocks == 1, "one 32-row block per wave");
+    // Sliding layers: each wave stages its 32 rows through its own 8.25 KB of the (now
+    // idle) ring, half the dims at a time, so that the stores write whole 256-byte row
+    // segments: a workgroup's short band leaves no time for scattered 16-byte pieces to
+    // merge into whole lines in L2 (written bytes dropped from 1.55x to 1x the output).
+    // Row pitch 264 bytes keeps the 8-byte writes of the 32 rows on distinct banks.
+    const int row = q0 + 32 * rb0 + r32;
+    const float l_tot = l_part[0] + __shfl_xor(l_part[0], 32);
+    const float gl = row < S ? bf16_to_f32(a.gate[((size_t)b * S + row) * kQHeads + hq]) : 0.0f;
+    const float scale = sigmoidf_fast(gl) / l_tot;
+    constexpr int kPitch = 264;
+    uint8_t* const stage = &s_ring[0][0][0] + wave * (32 * kPitch);   // 8 x 8448 B of 96 KB
 #pragma unroll
-  for (int rb = 0; rb < kRowBlocks; ++rb) {
-    const int row = q0 + 32 * (rb0 + rb) + r32;
-    const float l_tot = l_part[rb] + __shfl_xor(l_part[rb], 32);
-    if (row < S) {
-      const float gl = bf16_to_f32(a.gate[((size_t)b * S + row) * kQHeads + hq]);
-      const float scale = sigmoidf_fast(gl) / l_tot;
-      uint16_t* orow = a.out + (((size_t)b * S + row) * kQHeads + hq) * kHeadDim;
+    for (int r = 0; r < 2; ++r) {
 #pragma unroll
-      for (int db = 0; db < 8; ++db) {
+      for (int d4 = 0; d4 < 4; ++d4) {
+        const int db = 4 * r + d4;
 #pragma unroll
         for (int qd = 0; qd < 4; ++qd) {
           u32x2 w;
-          w[0] = pack_bf16x2(o[rb][db][4 * qd] * scale, o[rb][db][4 * qd + 1] * scale);
-          w[1] = pack_bf16x2(o[rb][db][4 * qd + 2] * scale, o[rb][db][4 * qd + 3] * scale);
-          *reinterpret_cast<u32x2*>(orow + 32 * db + 8 * qd + 4 * half) = w;
+          w[0] = pack_bf16x2(o[0][db][4 * qd] * scale, o[0][db][4 * qd + 1] * scale);
+          w[1] = pack_bf16x2(o[0][db][4 * qd + 2] * scale, o[0][db][4 * qd + 3] * scale);
+          *reinterpret_cast<u32x2*>(stage + r32 * kPitch + (32 * d4 + 8 * qd + 4 * half) * 2) = w;
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4));   // lgkmcnt(0): own writes
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int rr = 4 * i + (lane >> 4), c = lane & 15;   // row rr, 16-byte piece c
+        const u32x4 x = *reinterpret_cast<const u32x4*>(stage + rr * kPitch + c * 16);
+        const int grow = q0 + 32 * rb0 + rr;
+        if (grow < S)
+          *reinterpret_cast<u32x4*>(a.out + (((size_t)b * S + grow) * kQHeads + hq) * kHeadDim + 128 * r + 8 * c) = x;
+      }
+      __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4));   // reads done before reuse
+      __builtin_amdgcn_wave_barrier();
+    }
+  } else {
+#pragma unroll
+    for (int rb = 0; rb < kRowBlocks; ++rb) {
+      const int row = q0 + 32 * (rb0 + rb) + r32;
+      const float l_tot = l_part[rb] + __shfl_xor(l_part[rb], 32);
+      if (row < S) {
+        const float gl = bf16_to_f32(a.gate[((size_t)b * S + row) * kQHeads + hq]);
+        const float scale = sigmoidf_fast(gl) / l_tot;
+        uint16_t* orow = a.out + (((size_t)b * S + row) * kQHeads + hq) * kHeadDim;
+#pragma unroll
+        for (int db = 0; db < 8; ++db) {
+#pragma unroll
+          for (int qd = 0; qd < 4; ++qd) {
+            u32x2 w;
+            w[0] = pack_bf16x2(o[rb][db][4 * qd] * scale, o[rb][db][4 * qd + 1] * scale);
+            w[1] = pack_bf16x2(o[rb][db][4 * qd + 2] * scale, o[rb][db][4 * qd + 3] * scale);
+            *reinterpret_cast<u32x2*>(orow + 32 * db + 8 * qd + 4 * half) = w;
+          }
         }
       }
     }
