@@ -35,6 +35,7 @@ from .attention import (  # noqa: F401
     layer_type_of,
     layer_types,
     prefill,
+    prefill_chunk,
     rope,
     rope_inv_freq,
     round_to_bf16_bits,

@@ -204,6 +204,53 @@ def prefill(q, k, v, gate, layer_type, rows=None, *, theta=None, rot_dim=None,
     return out
 
 
+def prefill_chunk(q, k, v, gate, cache_k, cache_v, start_pos: int, layer_type, rows=None,
+                  row_block: int = 512) -> np.ndarray:
+    """Prefill of a chunk that continues a cached prefix: output at chunk rows ``rows``.
+
+    The chunk's token t sits at position P + t (P = ``start_pos``, the same for every
+    sequence).  Its keys are the cached prefix, read as stored (post-RoPE bf16 keys and
+    bf16 values: full layers positions 0..P-1 from slots 0..P-1, sliding layers positions
+    max(0, P-511)..P-1 from ring slots p mod 512 -- older ones are outside every chunk
+    query's window) followed by the chunk's own keys, rotated at their positions.  The
+    visibility rule is the same as for ``prefill`` over positions.  q [B,n,16,256],
+    k/v [B,n,4,256] (k before RoPE), gate [B,n,16], cache [B,cap,4,256]: bf16 bits.
+    Returns float64 [B, len(rows), 16, 256].  This is the step between prefill and decode
+    when a long context is fed in chunks or a prefix is reused ([F16Q4] section 一 and
+    [GGUF] section 四 on long contexts held in the KV cache).
+    """
+    th, rd, w = layer_params(layer_type)
+    q = np.asarray(q)
+    B, n, H, D = q.shape
+    Hk = np.asarray(k).shape[2]
+    P = int(start_pos)
+    if P < 0:
+        raise ValueError("start_pos must be >= 0")
+    rows = np.arange(n) if rows is None else np.asarray(rows, dtype=np.int64)
+    scale = softmax_scale(D)
+    h_lo = 0 if w is None else max(0, P - (w - 1))
+    h_pos = np.arange(h_lo, P)                                        # cached positions in reach
+    h_slot = np.array([cache_slot(int(p), layer_type) for p in h_pos], dtype=np.int64)
+    new_pos = P + np.arange(n)
+    kpos = np.concatenate([h_pos, new_pos])
+    out = np.zeros((B, len(rows), H, D), dtype=np.float64)
+    for b in range(B):
+        kr = np.concatenate([bf16_to_f64(np.asarray(cache_k)[b, h_slot]),
+                             rope(bf16_to_f64(k[b]), new_pos, th, rd)])    # [len(kpos), Hk, D]
+        vb = np.concatenate([bf16_to_f64(np.asarray(cache_v)[b, h_slot]), bf16_to_f64(v[b])])
+        for r0 in range(0, len(rows), row_block):
+            rr = rows[r0:r0 + row_block]
+            qpos = P + rr
+            vis = visibility(qpos, kpos, w)
+            qr = rope(bf16_to_f64(q[b, rr]), qpos, th, rd)
+            gb = np.asarray(gate)[b, rr]
+            for h in range(H):
+                g = kv_head_of(h, H, Hk)
+                out[b, r0:r0 + len(rr), h] = _attend(
+                    qr[:, h], kr[:, g], vb[:, g], vis, bf16_to_f64(gb[:, h]), scale)
+    return out
+
+
 def cache_slot(position: int, layer_type: int, window: int = WINDOW) -> int:
     """Cache slot of a position: itself on full layers, position mod 512 on sliding layers.
 

@@ -368,6 +368,93 @@ def pin_decode_matches_prefill_row(att):
         assert rel < 5e-3, f"decode vs prefill row lt={lt}: rel {rel:.2e}"
 
 
+# --------------------------------------------------------------------------- chunked prefill
+
+
+def _chunk_case(seed, P, n, lt, att):
+    """A sequence of P + n tokens whose first P sit in a cache written by the oracle's own
+    append (full cache of P + n slots, or the 512-slot ring)."""
+    inp = _small_inputs(seed, 1, P + n, 16, 4, 256)
+    cap = P + n if lt == att.FULL else 512
+    z = np.zeros((1, cap, 4, 256), np.uint16)
+    ck, cv = att.kv_append(z, z.copy(), inp["k"][:, :P], inp["v"][:, :P], np.array([0]), lt)
+    chunk = {name: inp[name][:, P:] for name in ("q", "k", "v", "gate")}
+    return inp, chunk, ck, cv
+
+
+def pin_chunk_start_zero_is_prefill(att):
+    """With no cached prefix a chunk is an ordinary prefill."""
+    inp = _small_inputs(31, 2, 37, 16, 4, 256)
+    for lt in (att.SLIDING, att.FULL):
+        z = np.zeros((2, 512, 4, 256), np.uint16)
+        got = att.prefill_chunk(inp["q"], inp["k"], inp["v"], inp["gate"], z, z, 0, lt)
+        _close(got, att.prefill(inp["q"], inp["k"], inp["v"], inp["gate"], lt), 1e-13, f"P=0 lt={lt}")
+
+
+def _brute_chunk(chunk, ck, cv, P, theta, rot_dim, window):
+    """Loop version: for each chunk query the explicit list of visible (position, key,
+    value) triples -- cached ones as stored, the chunk's own rotated through complex
+    numbers -- then one softmax per head."""
+    q, k, v, gate = (_f64(chunk[n][0]) for n in ("q", "k", "v", "gate"))
+    ck, cv = _f64(ck[0]), _f64(cv[0])
+    n = q.shape[0]
+    out = np.zeros((n, 16, 256))
+    for t in range(n):
+        qp = P + t
+        for h in range(16):
+            g = h // 4
+            qr = np.array(_rotate_complex(list(q[t, h]), float(qp), theta, rot_dim))
+            keys, vals = [], []
+            for p in range(qp + 1):
+                if window is not None and qp - p >= window:
+                    continue
+                if p < P:
+                    s = p if window is None else p % window
+                    keys.append(ck[s, g]); vals.append(cv[s, g])
+                else:
+                    keys.append(np.array(_rotate_complex(list(k[p - P, g]), float(p), theta, rot_dim)))
+                    vals.append(v[p - P, g])
+            sc = np.array([float(np.dot(qr, kk)) for kk in keys]) / 16.0
+            e = np.exp(sc - sc.max())
+            out[t, h] = (1.0 / (1.0 + math.exp(-gate[t, h]))) * (e @ np.array(vals)) / e.sum()
+    return out
+
+
+def pin_chunk_brute_force(att):
+    """Cached prefix plus chunk against the loop version: full cache and a ring that wraps."""
+    for lt, P, n, theta, rd, w in ((att.FULL, 40, 6, 5e6, 64, None), (att.SLIDING, 530, 5, 1e4, 256, 512)):
+        _, chunk, ck, cv = _chunk_case(32 + lt, P, n, lt, att)
+        got = att.prefill_chunk(chunk["q"], chunk["k"], chunk["v"], chunk["gate"], ck, cv, P, lt)
+        _close(got[0], _brute_chunk(chunk, ck, cv, P, theta, rd, w), 1e-11, f"chunk brute lt={lt}")
+
+
+def pin_chunk_ignores_out_of_reach_slots(att):
+    """Cache slots no chunk query can see do not change the result: on a full layer the
+    slots from P on, on a sliding layer the slot of position P-512 (one past the window of
+    the chunk's first query)."""
+    for lt, P, n, junk in ((att.FULL, 50, 4, slice(50, 54)), (att.SLIDING, 600, 4, (600 - 512) % 512)):
+        _, chunk, ck, cv = _chunk_case(34 + lt, P, n, lt, att)
+        base = att.prefill_chunk(chunk["q"], chunk["k"], chunk["v"], chunk["gate"], ck, cv, P, lt)
+        ck2, cv2 = ck.copy(), cv.copy()
+        ck2[0, junk] = 0x4120                      # bf16 10.0: would dominate any score
+        cv2[0, junk] = 0x4120
+        got = att.prefill_chunk(chunk["q"], chunk["k"], chunk["v"], chunk["gate"], ck2, cv2, P, lt)
+        _close(got, base, 0.0, f"out-of-reach slots lt={lt}")
+
+
+def pin_chunked_matches_one_shot(att):
+    """Feeding a sequence as prefix (appended to the cache) plus chunk gives the one-shot
+    prefill's rows, up to the bf16 rounding of the cached keys."""
+    for lt in (att.SLIDING, att.FULL):
+        P, n = 530, 70
+        inp, chunk, ck, cv = _chunk_case(36 + lt, P, n, lt, att)
+        got = att.prefill_chunk(chunk["q"], chunk["k"], chunk["v"], chunk["gate"], ck, cv, P, lt)
+        want = att.prefill(inp["q"], inp["k"], inp["v"], inp["gate"], lt, rows=np.arange(P, P + n))
+        rel = np.linalg.norm(got - want) / np.linalg.norm(want)
+        assert rel < 5e-3, f"chunked vs one-shot lt={lt}: rel {rel:.2e}"
+        assert np.max(np.abs(got - want)) < 2e-2, f"chunked vs one-shot lt={lt}: max abs"
+
+
 # --------------------------------------------------------------------------- footprint
 
 
@@ -400,4 +487,6 @@ ALL_PINS = [
     pin_zero_query_uniform_mean, pin_gate_limits, pin_gqa_equals_repeated_kv, pin_torch_sdpa,
     pin_rope_properties, pin_rope_frequencies, pin_layer_schedule, pin_bf16_rounding,
     pin_kv_append, pin_decode_brute, pin_decode_matches_prefill_row,
+    pin_chunk_start_zero_is_prefill, pin_chunk_brute_force, pin_chunk_ignores_out_of_reach_slots,
+    pin_chunked_matches_one_shot,
 ]

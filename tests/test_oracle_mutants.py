@@ -30,6 +30,10 @@ MUTANTS = {
     "decode_window_short": ("lo = 0 if w is None else max(0, L - w)", "lo = 0 if w is None else max(0, L - w + 1)"),
     "value_head_fixed": ("vb[:nk, g]", "vb[:nk, 0]"),
     "append_position_shift": ("p = int(pos[b]) + np.arange(n_new)", "p = int(pos[b]) + 1 + np.arange(n_new)"),
+    "chunk_query_positions": ("qpos = P + rr", "qpos = rr"),
+    "chunk_key_positions": ("new_pos = P + np.arange(n)", "new_pos = np.arange(n) + 1"),
+    "chunk_history_from_keys": ("bf16_to_f64(np.asarray(cache_v)[b, h_slot])", "bf16_to_f64(np.asarray(cache_k)[b, h_slot])"),
+    "chunk_history_one_short": ("h_pos = np.arange(h_lo, P)", "h_pos = np.arange(h_lo + 1, P)"),
 }
 
 
