@@ -141,8 +141,10 @@ def prefill_workspace_bytes(layer_type: int, batch: int, seq_len: int) -> int:
 
 def prefill(layer_type: int, q, k, v, gate, out=None, cache: KVCache | None = None,
             start_pos: int = 0, workspace=None, stream=None):
-    """spark_attn_prefill: q [B,S,16,256], k/v [B,S,4,256], gate [B,S,16] (bf16, pre-RoPE);
-    ``workspace`` (uint8, >= prefill_workspace_bytes) is allocated per call when omitted."""
+    """spark_attn_prefill: q [B,S,16,256], k/v [B,S,4,256], gate [B,S,16] (bf16, pre-RoPE)
+    of a chunk at positions start_pos .. start_pos+S-1 (start_pos > 0 reads the earlier
+    positions from ``cache``); ``workspace`` (uint8, >= prefill_workspace_bytes) is
+    allocated per call when omitted."""
     torch = _torch()
     B, S = int(q.shape[0]), int(q.shape[1])
     _check(q, "q", (B, S, N_Q_HEADS, HEAD_DIM), torch.bfloat16)

@@ -57,17 +57,18 @@ spark_status spark_attn_prefill(int32_t layer_type, int32_t batch, int32_t seq_l
   if (!valid_type(layer_type)) return SPARK_ERR_INVALID_ARG;
   if (batch < 1 || batch > kMaxBatch || seq_len < 1 || seq_len > kMaxSeq) return SPARK_ERR_INVALID_ARG;
   // The RoPE pass runs one thread per 16-byte K chunk, 128 per token, 256 per workgroup;
-  // the attention grid has ceil(seq_len / 48) * batch * 4 workgroups.
+  // the attention grid has ceil(seq_len / 64) * batch * 4 workgroups.
   if ((long long)batch * seq_len > 0xfffffffeLL) return SPARK_ERR_INVALID_ARG;
   if (!q || !k || !v || !gate_logits || !out) return SPARK_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned2(gate_logits))
     return SPARK_ERR_INVALID_ARG;
-  if (start_pos < 0) return SPARK_ERR_INVALID_ARG;
-  if (start_pos != 0) return SPARK_ERR_UNSUPPORTED;
+  if (start_pos < 0 || (long long)start_pos + seq_len > kMaxSeq) return SPARK_ERR_INVALID_ARG;
+  if (start_pos > 0 && !cache) return SPARK_ERR_INVALID_ARG;   // the prefix is read from the cache
   if (cache) {
     const spark_status cs = check_cache(layer_type, cache, batch);
     if (cs != SPARK_OK) return cs;
-    if (layer_type == SPARK_LAYER_FULL && cache->capacity < seq_len) return SPARK_ERR_INVALID_ARG;
+    if (layer_type == SPARK_LAYER_FULL && (long long)cache->capacity < (long long)start_pos + seq_len)
+      return SPARK_ERR_INVALID_ARG;
   }
   if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u)) return SPARK_ERR_INVALID_ARG;
   if (workspace_bytes < spark::prefill_workspace_bytes(batch, seq_len)) return SPARK_ERR_WORKSPACE;
@@ -87,6 +88,7 @@ spark_status spark_attn_prefill(int32_t layer_type, int32_t batch, int32_t seq_l
   a.seq_len = seq_len;
   a.cache_cap = cache ? cache->capacity : 0;
   a.nqb = (int)nqb;
+  a.start_pos = start_pos;
   return from_hip(spark::launch_prefill(layer_type, a, static_cast<hipStream_t>(stream)));
 }
 

@@ -102,55 +102,67 @@ __device__ __forceinline__ void barrier_lds() {
 constexpr int kKLoads = 16 / kWaves;              // K-tile load instructions per wave
 constexpr int kVLoads = 16 / kWaves;              // V-tile load instructions per wave
 
-// Start loading tile (keys k0 .. k0+31) of (sequence b, KV head g): K from the rotated
-// keys.  Instruction n of K brings chunks 2n, 2n+1 of all 32 keys; instruction n of V rows
-// 2n, 2n+1 with chunk positions swizzled by 4 * (row % 4).  Rows past the end load row
-// S-1 (masked later).
+// Global rows of key position p (p < P + n) of (sequence b, KV head g): the cached prefix
+// for p < P (slot p, or ring slot p mod 512 on a sliding layer), else the chunk's keys as
+// rotated by the RoPE pass and its values.
+template <int LT>
+__device__ __forceinline__ size_t prefix_row(const PrefillArgs& a, int b, int g, int p) {
+  const int slot = LT == kFull ? p : (p & (kWindow - 1));
+  return (((size_t)b * a.cache_cap + slot) * kKvHeads + g) * kHeadDim;
+}
+__device__ __forceinline__ size_t chunk_row(const PrefillArgs& a, int b, int g, int p) {
+  return (((size_t)b * a.seq_len + (p - a.start_pos)) * kKvHeads + g) * kHeadDim;
+}
+
+// Load instruction i of tile (keys k0 .. k0+31, absolute positions) of (sequence b, KV
+// head g).  Instruction n of K brings chunks 2n, 2n+1 of all 32 keys; instruction n of V
+// rows 2n, 2n+1 with chunk positions swizzled by 4 * (row % 4).  Rows past the chunk's
+// end load its last key (masked later).  A tile wholly inside the prefix or wholly inside
+// the chunk picks its source once; only a tile across the boundary selects per lane.
+template <int LT>
 __device__ __forceinline__ void issue_one(const PrefillArgs& a, int b, int g, int k0, int wave,
                                           int lane, uint8_t* ks, uint8_t* vs, int i) {
-  const int S = a.seq_len;
-  const size_t seq_row0 = (size_t)b * S;
+  const int P = a.start_pos;
+  const int kend = P + a.seq_len;
+  const bool in_chunk = k0 >= P, in_prefix = k0 + kBN <= P;   // wave-uniform
   if (i < kKLoads) {
-    const int pk = min(k0 + (lane & 31), S - 1);
+    const int pk = min(k0 + (lane & 31), kend - 1);
     const int n = kKLoads * wave + i;
-    const int chunk = 2 * n + (lane >> 5);
-    dma16(a.k_rot + ((seq_row0 + pk) * kKvHeads + g) * kHeadDim + 8 * chunk, ks + n * 1024);
+    const int off = 8 * (2 * n + (lane >> 5));
+    const uint16_t* src;
+    if (in_chunk) src = a.k_rot + chunk_row(a, b, g, pk);
+    else if (in_prefix) src = a.cache_k + prefix_row<LT>(a, b, g, pk);
+    else src = pk < P ? a.cache_k + prefix_row<LT>(a, b, g, pk) : a.k_rot + chunk_row(a, b, g, pk);
+    dma16(src + off, ks + n * 1024);
   } else {
     const int n = kVLoads * wave + (i - kKLoads);
     const int r = 2 * n + (lane >> 5);
-    const int chunk = (lane & 31) ^ (4 * (r & 3));
-    const int p = min(k0 + r, S - 1);
-    dma16(a.v + ((seq_row0 + p) * kKvHeads + g) * kHeadDim + 8 * chunk, vs + n * 1024);
+    const int off = 8 * ((lane & 31) ^ (4 * (r & 3)));
+    const int p = min(k0 + r, kend - 1);
+    const uint16_t* src;
+    if (in_chunk) src = a.v + chunk_row(a, b, g, p);
+    else if (in_prefix) src = a.cache_v + prefix_row<LT>(a, b, g, p);
+    else src = p < P ? a.cache_v + prefix_row<LT>(a, b, g, p) : a.v + chunk_row(a, b, g, p);
+    dma16(src + off, vs + n * 1024);
   }
 }
+template <int LT>
 __device__ __forceinline__ void issue_tile(const PrefillArgs& a, int b, int g, int k0, int wave,
                                            int lane, uint8_t* ks, uint8_t* vs) {
-  const int S = a.seq_len;
-  const size_t seq_row0 = (size_t)b * S;
-  const int pk = min(k0 + (lane & 31), S - 1);
 #pragma unroll
-  for (int q = 0; q < kKLoads; ++q) {
-    const int n = kKLoads * wave + q;
-    const int chunk = 2 * n + (lane >> 5);
-    dma16(a.k_rot + ((seq_row0 + pk) * kKvHeads + g) * kHeadDim + 8 * chunk, ks + n * 1024);
-  }
-#pragma unroll
-  for (int q = 0; q < kVLoads; ++q) {
-    const int n = kVLoads * wave + q;
-    const int r = 2 * n + (lane >> 5);
-    const int chunk = (lane & 31) ^ (4 * (r & 3));
-    const int p = min(k0 + r, S - 1);
-    dma16(a.v + ((seq_row0 + p) * kKvHeads + g) * kHeadDim + 8 * chunk, vs + n * 1024);
-  }
+  for (int i = 0; i < kKLoads + kVLoads; ++i) issue_one<LT>(a, b, g, k0, wave, lane, ks, vs, i);
 }
 
-// RoPE of K, once per position: k_rot = R_p(k) (rotate-half form: pair (m, m + r/2) is
-// rotated by angle p * theta^(-2m/r) for m < r/2; dims >= r are copied), and, when a cache
-// is given, the rotated keys and the values into their cache slots (full layer: slot p;
-// sliding layer: slot p mod 512 for the last 512 positions) -- Spark-X2.6-4B-Base hybrid
-// attention explainer, eliteato.com/news/34565, sections "全局注意力 5M 基频 RoPE" and
-// "滑动窗口 512".  One thread per 16-byte chunk of a K row: a rotary chunk also reads its
-// partner chunk (dims + or - r/2) and computes its own half of the pair.
+// RoPE of the chunk's K, once per position p = P + t: k_rot = R_p(k) (rotate-half form:
+// pair (m, m + r/2) is rotated by angle p * theta^(-2m/r) for m < r/2; dims >= r are
+// copied), and, when a cache is given, the rotated keys and the values into their cache
+// slots (full layer: slot p; sliding layer: slot p mod 512 for the last 512 positions,
+// here only when there is no cached prefix -- otherwise those slots still hold keys the
+// chunk's first queries read, and the ring is written after the attention) --
+// Spark-X2.6-4B-Base hybrid attention explainer, eliteato.com/news/34565, sections
+// "全局注意力 5M 基频 RoPE" and "滑动窗口 512".  One thread per 16-byte chunk of a K row: a
+// rotary chunk also reads its partner chunk (dims + or - r/2) and computes its own half of
+// the pair.
 template <int LT>
 __global__ __launch_bounds__(256) void prefill_rope_kernel(PrefillArgs a) {
   using T = LayerTraits<LT>;
@@ -163,7 +175,7 @@ __global__ __launch_bounds__(256) void prefill_rope_kernel(PrefillArgs a) {
   const size_t row = idx >> 5;                       // (b * S + p) * 4 + g
   const int c = (int)(idx & 31);
   if (row >= nrows) return;
-  const int p = (int)((row / kKvHeads) % a.seq_len);
+  const int p = a.start_pos + (int)((row / kKvHeads) % a.seq_len);
   const uint16_t* krow = a.k + row * kHeadDim;
   const u32x4 x = ld_global16(krow + 8 * c);
   u32x4 y = x;
@@ -183,7 +195,7 @@ __global__ __launch_bounds__(256) void prefill_rope_kernel(PrefillArgs a) {
     }
   }
   st_global16(a.k_rot + row * kHeadDim + 8 * c, y);
-  if (a.cache_k != nullptr && (LT == kFull || p >= a.seq_len - kWindow)) {
+  if (a.cache_k != nullptr && (LT == kFull || (a.start_pos == 0 && p >= a.seq_len - kWindow))) {
     const int slot = LT == kFull ? p : (p & (kWindow - 1));
     const size_t b = row / ((size_t)kKvHeads * a.seq_len);
     const int g = (int)(row % kKvHeads);
@@ -191,6 +203,27 @@ __global__ __launch_bounds__(256) void prefill_rope_kernel(PrefillArgs a) {
     st_global16(a.cache_k + dst, y);
     st_global16(a.cache_v + dst, ld_global16(a.v + row * kHeadDim + 8 * c));
   }
+}
+
+// Sliding layer after a chunk that continues a prefix: the chunk's last 512 positions
+// into their ring slots (p mod 512), once the attention has read the prefix's keys there.
+// One thread per 16-byte chunk of those rows' K and V.
+__global__ __launch_bounds__(256) void prefill_ring_kernel(PrefillArgs a) {
+  const int n = a.seq_len;
+  const int t0 = n > kWindow ? n - kWindow : 0;       // first chunk row kept
+  const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const size_t per_seq = (size_t)(n - t0) * kKvHeads * 32;
+  if (idx >= (size_t)a.batch * per_seq) return;
+  const int b = (int)(idx / per_seq);
+  const size_t r = idx % per_seq;
+  const int t = t0 + (int)(r / (kKvHeads * 32));
+  const int g = (int)((r / 32) % kKvHeads);
+  const int c = (int)(r % 32);
+  const int slot = (a.start_pos + t) & (kWindow - 1);
+  const size_t src = (((size_t)b * n + t) * kKvHeads + g) * kHeadDim + 8 * c;
+  const size_t dst = (((size_t)b * a.cache_cap + slot) * kKvHeads + g) * kHeadDim + 8 * c;
+  st_global16(a.cache_k + dst, ld_global16(a.k_rot + src));
+  st_global16(a.cache_v + dst, ld_global16(a.v + src));
 }
 
 // Workgroup -> (sequence, KV head, query block).  Workgroups are dealt round-robin to the
@@ -231,7 +264,7 @@ __device__ __forceinline__ void load_q(const PrefillArgs& a, int b, int hq, int 
 #pragma unroll
     for (int s = 0; s < 16; ++s) raw[s] = u32x4{0, 0, 0, 0};
   }
-  const double p = (double)row;
+  const double p = (double)(a.start_pos + row);   // the row's position
   constexpr int kPairChunks = T::kRot / 32;         // fragment s pairs with s + kPairChunks
 #pragma unroll
   for (int s = 0; s < 16; ++s) {
@@ -279,7 +312,8 @@ void prefill_kernel(PrefillArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // scalar: wave-uniform branches
   const int half = lane >> 5;
   const int r32 = lane & 31;
-  const int S = a.seq_len;
+  const int S = a.seq_len;                  // chunk rows
+  const int P = a.start_pos;                // position of chunk row 0
 
   int b, g, qb;
   block_coords<LT>(blockIdx.x, a.batch, a.nqb, b, g, qb);
@@ -287,14 +321,14 @@ void prefill_kernel(PrefillArgs a) {
   const int hq = g * kGroup + (kRowBlocks == 2 ? wave : wave >> 1);
   const int rb0 = kRowBlocks == 2 ? 0 : (wave & 1);      // first 32-row block of this wave
 
-  const int hi_key = min(q0 + kBM - 1, S - 1);
-  const int lo_key = T::kWindowed ? max(0, q0 - (kWindow - 1)) : 0;
+  const int hi_key = P + min(q0 + kBM - 1, S - 1);                 // absolute key positions
+  const int lo_key = T::kWindowed ? max(0, P + q0 - (kWindow - 1)) : 0;
   const int kt_lo = lo_key / kBN;
   const int kt_hi = hi_key / kBN;
 
   // Start streaming the first two tiles before anything else.
-  issue_tile(a, b, g, kt_lo * kBN, wave, lane, s_k0, s_v0);
-  if (kt_lo + 1 <= kt_hi) issue_tile(a, b, g, (kt_lo + 1) * kBN, wave, lane, s_k1, s_v1);
+  issue_tile<LT>(a, b, g, kt_lo * kBN, wave, lane, s_k0, s_v0);
+  if (kt_lo + 1 <= kt_hi) issue_tile<LT>(a, b, g, (kt_lo + 1) * kBN, wave, lane, s_k1, s_v1);
 
   if (tid < T::kRot / 2) s_inv[tid] = rope_inv_rev(tid, T::kRot, log2(T::kTheta));
   barrier_lds();
@@ -345,7 +379,7 @@ void prefill_kernel(PrefillArgs a) {
     bool any[kRowBlocks], edge[kRowBlocks], any_rb = false;
 #pragma unroll
     for (int rb = 0; rb < kRowBlocks; ++rb) {
-      const int r0 = q0 + 32 * (rb0 + rb);
+      const int r0 = P + q0 + 32 * (rb0 + rb);   // position of the block's first row
       any[rb] = (k0 <= r0 + 31) && (!T::kWindowed || k0 + kBN - 1 >= r0 - (kWindow - 1));
       edge[rb] = (k0 + kBN - 1 > r0) || (T::kWindowed && k0 < r0 + 31 - (kWindow - 1));
       any_rb = any_rb || any[rb];
@@ -359,17 +393,18 @@ void prefill_kernel(PrefillArgs a) {
         const bf16x8 ka = as_bf16x8(*reinterpret_cast<const u32x4*>(ks + (32 * (2 * s + half) + r32) * 16));
 #pragma unroll
         for (int rb = 0; rb < kRowBlocks; ++rb) sacc[rb] = mfma_32x32x16(ka, qf[rb][s], sacc[rb]);
-        if (ST != 0 && two_ahead && (s & 3) == 1) issue_one(a, b, g, k0 + 2 * kBN, wave, lane, ks2, vs2, s >> 2);
+        if (ST != 0 && two_ahead && (s & 3) == 1) issue_one<LT>(a, b, g, k0 + 2 * kBN, wave, lane, ks2, vs2, s >> 2);
       }
       bf16x8 pf[kRowBlocks][2];
 #pragma unroll
       for (int rb = 0; rb < kRowBlocks; ++rb) {
         const int row = q0 + 32 * (rb0 + rb) + r32;
+        const int rpos = P + row;                 // this lane's query position
         if (edge[rb]) {
 #pragma unroll
           for (int v = 0; v < 16; ++v) {
             const int key = k0 + 8 * (v >> 2) + 4 * half + (v & 3);
-            const bool vis = key <= row && (!T::kWindowed || key > row - kWindow);
+            const bool vis = key <= rpos && (!T::kWindowed || key > rpos - kWindow);
             sacc[rb][v] = vis ? sacc[rb][v] : -INFINITY;
           }
         }
@@ -414,7 +449,7 @@ void prefill_kernel(PrefillArgs a) {
     }
     // Step 0 issues its prefetch after the MFMAs; the others issue it one instruction every
     // four QK MFMAs, or here when this wave's rows see no key of the tile.
-    if (two_ahead && (ST == 0 || !any_rb)) issue_tile(a, b, g, k0 + 2 * kBN, wave, lane, ks2, vs2);
+    if (two_ahead && (ST == 0 || !any_rb)) issue_tile<LT>(a, b, g, k0 + 2 * kBN, wave, lane, ks2, vs2);
     if (kt + 1 <= kt_hi) {
       // This lane's loads of tile kt+1 were issued one step ago; tile kt+2's may still be
       // in flight.  Every lane waits for its own loads before the barrier: other waves
@@ -507,6 +542,11 @@ hipError_t launch_prefill(int layer_type, const PrefillArgs& a, hipStream_t stre
   if (layer_type == kSliding) {
     hipLaunchKernelGGL(prefill_rope_kernel<kSliding>, rope_grid, dim3(256), 0, stream, a);
     hipLaunchKernelGGL(prefill_kernel<kSliding>, dim3(blocks), dim3(kThreads), 0, stream, a);
+    if (a.start_pos > 0 && a.cache_k != nullptr) {
+      const int kept = a.seq_len < kWindow ? a.seq_len : kWindow;
+      const size_t n = (size_t)a.batch * kept * kKvHeads * 32;
+      hipLaunchKernelGGL(prefill_ring_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, a);
+    }
   } else {
     hipLaunchKernelGGL(prefill_rope_kernel<kFull>, rope_grid, dim3(256), 0, stream, a);
     hipLaunchKernelGGL(prefill_kernel<kFull>, dim3(blocks), dim3(kThreads), 0, stream, a);

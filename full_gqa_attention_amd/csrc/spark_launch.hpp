@@ -20,6 +20,7 @@ struct PrefillArgs {
   int seq_len;
   int cache_cap;
   int nqb;                // query blocks per sequence
+  int start_pos;          // position of the chunk's first token; > 0: prefix in the cache
 };
 
 struct AppendArgs {

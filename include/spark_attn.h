@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define SPARK_ATTN_ABI_VERSION 3
+#define SPARK_ATTN_ABI_VERSION 4
 
 enum { SPARK_Q_HEADS = 16, SPARK_KV_HEADS = 4, SPARK_HEAD_DIM = 256, SPARK_WINDOW = 512 };
 
@@ -85,23 +85,30 @@ typedef struct spark_kv_cache {
 size_t spark_attn_prefill_workspace_bytes(int32_t layer_type, int32_t batch, int32_t seq_len);
 
 /*
- * Prefill: attention of `seq_len` new tokens per sequence over themselves, one layer.
+ * Prefill: attention of a chunk of `seq_len` new tokens per sequence, one layer, over
+ * the chunk itself and, when start_pos > 0, over the start_pos earlier tokens already
+ * in the cache (chunked prefill).  Token t of a sequence sits at position start_pos + t
+ * and sees the keys at positions <= start_pos + t (SLIDING: the last 512 of them).
  *   q            bf16 [batch, seq_len, 16, 256], before RoPE
  *   k, v         bf16 [batch, seq_len, 4, 256], k before RoPE
  *   gate_logits  bf16 [batch, seq_len, 16]
- *   cache        optional (NULL = none): receives the rotated keys and the values of
- *                positions 0..seq_len-1 (SLIDING: only the last 512 of them, in their
- *                ring slots).  cache->batch must equal batch; FULL needs
- *                capacity >= seq_len.
+ *   cache        optional when start_pos == 0 (NULL = none), required otherwise.  Read:
+ *                positions 0..start_pos-1 (FULL, slot p) or max(0, start_pos-512) ..
+ *                start_pos-1 (SLIDING, slot p mod 512), as spark_kv_append or an earlier
+ *                prefill left them.  Written: the chunk's rotated keys and values at
+ *                positions start_pos .. start_pos+seq_len-1 (SLIDING: only the last 512
+ *                of them, in their ring slots).  cache->batch must equal batch; FULL
+ *                needs capacity >= start_pos + seq_len.
  *   workspace    device scratch of at least spark_attn_prefill_workspace_bytes(...)
  *                bytes, 256-byte aligned, used only during the call (calls sharing one
  *                workspace must be ordered on a stream); SPARK_ERR_WORKSPACE if smaller
  *   out          bf16 [batch, seq_len, 16, 256] (written)
- *   start_pos    position of the first token; only 0 is supported (SPARK_ERR_UNSUPPORTED
- *                otherwise).
- * Token t of a sequence sits at position start_pos + t.  1 <= seq_len <= 2^20,
- * 1 <= batch <= 65535, batch * seq_len < 2^32.  Two launches: RoPE of K into the
- * workspace (and the cache writes), then the attention with the sigmoid head gate.
+ *   start_pos    position of the chunk's first token, 0 <= start_pos, start_pos +
+ *                seq_len <= 2^20; every sequence of the batch starts at it.
+ * 1 <= seq_len <= 2^20, 1 <= batch <= 65535, batch * seq_len < 2^32.  Launches: RoPE of
+ * K into the workspace (and the cache writes), then the attention with the sigmoid head
+ * gate; a SLIDING chunk with start_pos > 0 writes its ring slots in a third launch, after
+ * the attention has read the prefix from them.
  */
 spark_status spark_attn_prefill(int32_t layer_type, int32_t batch, int32_t seq_len,
                                 int32_t start_pos, const void* q, const void* k,

@@ -30,7 +30,7 @@ def test_exports_every_declared_function():
 
 
 def test_version_and_status_strings():
-    assert fga.abi_version() == 3
+    assert fga.abi_version() == 4
     assert fga.status_string(0) == "ok"
     assert fga.status_string(3) == "workspace too small"
     assert fga.status_string(99) == "unknown status"
@@ -51,7 +51,10 @@ def prefill(**kw):
 @pytest.mark.parametrize("kw,status", [
     (dict(lt=2), 1), (dict(lt=-1), 1), (dict(B=0), 1), (dict(S=0), 1), (dict(S=(1 << 20) + 1), 1),
     (dict(q=None), 1), (dict(out=None), 1), (dict(k=MISALIGNED), 1), (dict(start=-1), 1),
-    (dict(start=5), 2),
+    (dict(start=5), 1),                       # a prefix needs the cache it is read from
+    (dict(start=16, cache=_cache(cap=31)), 1),   # full: capacity < start_pos + seq_len
+    (dict(start=(1 << 20) - 15, cache=_cache(cap=1 << 21)), 1),   # start_pos + seq_len > 2^20
+    (dict(lt=0, start=100, cache=_cache(batch=2)), 1),
     (dict(lt=0, cache=_cache(cap=511)), 1), (dict(lt=1, cache=_cache(cap=15)), 1),
     (dict(cache=_cache(batch=2)), 1), (dict(cache=_cache(k=None)), 1),
     (dict(ws=None), 1), (dict(ws=MISALIGNED), 1),

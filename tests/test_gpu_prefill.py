@@ -118,9 +118,12 @@ def test_prefill_rejects_bad_arguments(fga):
     q = torch.zeros(1, 8, 16, 256, dtype=torch.bfloat16, device="cuda")
     k = torch.zeros(1, 8, 4, 256, dtype=torch.bfloat16, device="cuda")
     g = torch.zeros(1, 8, 16, dtype=torch.bfloat16, device="cuda")
-    with pytest.raises(fga.SparkError) as e:
+    with pytest.raises(fga.SparkError) as e:      # a prefix is read from a cache
         fga.prefill(oracle.FULL, q, k, k, g, start_pos=3)
-    assert e.value.status == 2
+    assert e.value.status == 1
+    with pytest.raises(fga.SparkError) as e:      # capacity < start_pos + seq_len
+        fga.prefill(oracle.FULL, q, k, k, g, cache=fga.KVCache(oracle.FULL, 1, 10), start_pos=3)
+    assert e.value.status == 1
     cache = fga.KVCache(oracle.FULL, 1, 4)
     with pytest.raises(fga.SparkError) as e:
         fga.prefill(oracle.FULL, q, k, k, g, cache=cache)
