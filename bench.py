@@ -131,7 +131,8 @@ def sliding_pairs(S):
 
 def bench_configs(fga, synth):
     """The other workloads of the hot path's scope table, each timed on its own:
-    sliding prefill S=1024; the 36-layer stack at S=32768; batched decode (full, cold
+    sliding prefill S=1024; a chunk of 8192 after a cached prefix of 8192 (both layer
+    types); the 36-layer stack at S=32768; batched decode (full, cold
     caches; sliding ring, warm and cold); long decode at 128K and 1M tokens."""
     import numpy as np
     import torch
@@ -150,6 +151,27 @@ def bench_configs(fga, synth):
                                     "tokens_per_s": S / (ms * 1e-3)}
     log(f"config 1 sliding prefill S=1024: {ms * 1e3:.1f} us  {tf:.0f} TFLOP/s")
     del q, k, v, g, o, ws
+
+    # Chunked prefill: a chunk of 8192 tokens after a cached prefix of 8192, batch 1, each
+    # layer type (the prefix's keys are read from the cache, device-drawn N(0,1)).
+    P = n = 8192
+    gen.manual_seed(synth.CONFIG_SEED[2] + 100)
+    q, k, v, g = (dev_normal(gen, (1, n, 16, 256)), dev_normal(gen, (1, n, 4, 256)),
+                  dev_normal(gen, (1, n, 4, 256)), dev_normal(gen, (1, n, 16)))
+    o = torch.empty_like(q)
+    for lt, name in ((fga.FULL, "full"), (fga.SLIDING, "sliding")):
+        cap = P + n if lt == fga.FULL else 512
+        cache = fga.KVCache(lt, 1, cap, k=dev_normal(gen, (1, cap, 4, 256)), v=dev_normal(gen, (1, cap, 4, 256)))
+        ws = torch.empty(fga.prefill_workspace_bytes(lt, 1, n), dtype=torch.uint8, device="cuda")
+        ms = time_launches(lambda: fga.prefill(lt, q, k, v, g, out=o, cache=cache, start_pos=P,
+                                               workspace=ws), 100, 20)
+        pairs = n * P + n * (n + 1) // 2 if lt == fga.FULL else n * 512
+        tf = 16384 * pairs / (ms * 1e-3) / 1e12
+        out[f"chunk_prefill_{name}_p8192_n8192"] = {"ms": ms, "tflops": tf, "frac_mfma": tf / PEAK_BF16_TFLOPS,
+                                                    "tokens_per_s": n / (ms * 1e-3)}
+        log(f"chunked prefill {name} P=8192 n=8192: {ms:.3f} ms  {tf:.0f} TFLOP/s")
+        del cache, ws
+    del q, k, v, g, o
 
     # Config 4: 36-layer stack, batch 1, S = 32768, independent inputs per layer (drawn on
     # the device: 24 GB of N(0,1) bf16); layer l is full iff l % 4 == 3.

@@ -110,8 +110,8 @@ __device__ __forceinline__ size_t prefix_row(const PrefillArgs& a, int b, int g,
   const int slot = LT == kFull ? p : (p & (kWindow - 1));
   return (((size_t)b * a.cache_cap + slot) * kKvHeads + g) * kHeadDim;
 }
-__device__ __forceinline__ size_t chunk_row(const PrefillArgs& a, int b, int g, int p) {
-  return (((size_t)b * a.seq_len + (p - a.start_pos)) * kKvHeads + g) * kHeadDim;
+__device__ __forceinline__ size_t chunk_row(const PrefillArgs& a, int b, int g, int p, int P) {
+  return (((size_t)b * a.seq_len + (p - P)) * kKvHeads + g) * kHeadDim;
 }
 
 // Load instruction i of tile (keys k0 .. k0+31, absolute positions) of (sequence b, KV
@@ -119,38 +119,37 @@ __device__ __forceinline__ size_t chunk_row(const PrefillArgs& a, int b, int g, 
 // rows 2n, 2n+1 with chunk positions swizzled by 4 * (row % 4).  Rows past the chunk's
 // end load its last key (masked later).  A tile wholly inside the prefix or wholly inside
 // the chunk picks its source once; only a tile across the boundary selects per lane.
-template <int LT>
+// PFX = false: no prefix (start_pos == 0), every key comes from the chunk.
+template <int LT, bool PFX>
 __device__ __forceinline__ void issue_one(const PrefillArgs& a, int b, int g, int k0, int wave,
                                           int lane, uint8_t* ks, uint8_t* vs, int i) {
-  const int P = a.start_pos;
+  const int P = PFX ? a.start_pos : 0;
   const int kend = P + a.seq_len;
-  const bool in_chunk = k0 >= P, in_prefix = k0 + kBN <= P;   // wave-uniform
+  const bool in_chunk = !PFX || k0 >= P, in_prefix = k0 + kBN <= P;   // wave-uniform
   if (i < kKLoads) {
     const int pk = min(k0 + (lane & 31), kend - 1);
     const int n = kKLoads * wave + i;
     const int off = 8 * (2 * n + (lane >> 5));
-    const uint16_t* src;
-    if (in_chunk) src = a.k_rot + chunk_row(a, b, g, pk);
-    else if (in_prefix) src = a.cache_k + prefix_row<LT>(a, b, g, pk);
-    else src = pk < P ? a.cache_k + prefix_row<LT>(a, b, g, pk) : a.k_rot + chunk_row(a, b, g, pk);
-    dma16(src + off, ks + n * 1024);
+    const bool from_cache = !in_chunk && (in_prefix || pk < P);
+    const uint16_t* base = from_cache ? a.cache_k : a.k_rot;
+    const size_t row = from_cache ? prefix_row<LT>(a, b, g, pk) : chunk_row(a, b, g, pk, P);
+    dma16(base + (row + off), ks + n * 1024);
   } else {
     const int n = kVLoads * wave + (i - kKLoads);
     const int r = 2 * n + (lane >> 5);
     const int off = 8 * ((lane & 31) ^ (4 * (r & 3)));
     const int p = min(k0 + r, kend - 1);
-    const uint16_t* src;
-    if (in_chunk) src = a.v + chunk_row(a, b, g, p);
-    else if (in_prefix) src = a.cache_v + prefix_row<LT>(a, b, g, p);
-    else src = p < P ? a.cache_v + prefix_row<LT>(a, b, g, p) : a.v + chunk_row(a, b, g, p);
-    dma16(src + off, vs + n * 1024);
+    const bool from_cache = !in_chunk && (in_prefix || p < P);
+    const uint16_t* base = from_cache ? a.cache_v : a.v;
+    const size_t row = from_cache ? prefix_row<LT>(a, b, g, p) : chunk_row(a, b, g, p, P);
+    dma16(base + (row + off), vs + n * 1024);
   }
 }
-template <int LT>
+template <int LT, bool PFX>
 __device__ __forceinline__ void issue_tile(const PrefillArgs& a, int b, int g, int k0, int wave,
                                            int lane, uint8_t* ks, uint8_t* vs) {
 #pragma unroll
-  for (int i = 0; i < kKLoads + kVLoads; ++i) issue_one<LT>(a, b, g, k0, wave, lane, ks, vs, i);
+  for (int i = 0; i < kKLoads + kVLoads; ++i) issue_one<LT, PFX>(a, b, g, k0, wave, lane, ks, vs, i);
 }
 
 // RoPE of the chunk's K, once per position p = P + t: k_rot = R_p(k) (rotate-half form:
@@ -251,8 +250,8 @@ __device__ __forceinline__ void block_coords(int id, int batch, int nqb, int& b,
 // Rotate (RoPE at position p) and scale the Q row slice this lane holds, into MFMA
 // B-operand fragments: fragment s holds dims 16s + 8*half + j.
 template <int LT>
-__device__ __forceinline__ void load_q(const PrefillArgs& a, int b, int hq, int row, int half,
-                                       const double* inv, bf16x8* qf) {
+__device__ __forceinline__ void load_q(const PrefillArgs& a, int b, int hq, int row, int pos0,
+                                       int half, const double* inv, bf16x8* qf) {
   using T = LayerTraits<LT>;
   const int S = a.seq_len;
   u32x4 raw[16];
@@ -264,7 +263,7 @@ __device__ __forceinline__ void load_q(const PrefillArgs& a, int b, int hq, int 
 #pragma unroll
     for (int s = 0; s < 16; ++s) raw[s] = u32x4{0, 0, 0, 0};
   }
-  const double p = (double)(a.start_pos + row);   // the row's position
+  const double p = (double)(pos0 + row);   // the row's position
   constexpr int kPairChunks = T::kRot / 32;         // fragment s pairs with s + kPairChunks
 #pragma unroll
   for (int s = 0; s < 16; ++s) {
@@ -293,7 +292,7 @@ __device__ __forceinline__ void load_q(const PrefillArgs& a, int b, int hq, int 
   }
 }
 
-template <int LT>
+template <int LT, bool PFX>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves / 4, kWaves / 4)))
 void prefill_kernel(PrefillArgs a) {
   using T = LayerTraits<LT>;
@@ -313,7 +312,7 @@ void prefill_kernel(PrefillArgs a) {
   const int half = lane >> 5;
   const int r32 = lane & 31;
   const int S = a.seq_len;                  // chunk rows
-  const int P = a.start_pos;                // position of chunk row 0
+  const int P = PFX ? a.start_pos : 0;      // position of chunk row 0
 
   int b, g, qb;
   block_coords<LT>(blockIdx.x, a.batch, a.nqb, b, g, qb);
@@ -327,8 +326,8 @@ void prefill_kernel(PrefillArgs a) {
   const int kt_hi = hi_key / kBN;
 
   // Start streaming the first two tiles before anything else.
-  issue_tile<LT>(a, b, g, kt_lo * kBN, wave, lane, s_k0, s_v0);
-  if (kt_lo + 1 <= kt_hi) issue_tile<LT>(a, b, g, (kt_lo + 1) * kBN, wave, lane, s_k1, s_v1);
+  issue_tile<LT, PFX>(a, b, g, kt_lo * kBN, wave, lane, s_k0, s_v0);
+  if (kt_lo + 1 <= kt_hi) issue_tile<LT, PFX>(a, b, g, (kt_lo + 1) * kBN, wave, lane, s_k1, s_v1);
 
   if (tid < T::kRot / 2) s_inv[tid] = rope_inv_rev(tid, T::kRot, log2(T::kTheta));
   barrier_lds();
@@ -336,7 +335,7 @@ void prefill_kernel(PrefillArgs a) {
   // Q fragments of both 32-row blocks: lane holds row r32 of each.
   bf16x8 qf[kRowBlocks][16];
 #pragma unroll
-  for (int rb = 0; rb < kRowBlocks; ++rb) load_q<LT>(a, b, hq, q0 + 32 * (rb0 + rb) + r32, half, s_inv, qf[rb]);
+  for (int rb = 0; rb < kRowBlocks; ++rb) load_q<LT>(a, b, hq, q0 + 32 * (rb0 + rb) + r32, P, half, s_inv, qf[rb]);
 
   // First tiles: wait for this lane's loads (of both), publish.
   wait_vmcnt<0>();
@@ -393,7 +392,7 @@ void prefill_kernel(PrefillArgs a) {
         const bf16x8 ka = as_bf16x8(*reinterpret_cast<const u32x4*>(ks + (32 * (2 * s + half) + r32) * 16));
 #pragma unroll
         for (int rb = 0; rb < kRowBlocks; ++rb) sacc[rb] = mfma_32x32x16(ka, qf[rb][s], sacc[rb]);
-        if (ST != 0 && two_ahead && (s & 3) == 1) issue_one<LT>(a, b, g, k0 + 2 * kBN, wave, lane, ks2, vs2, s >> 2);
+        if (ST != 0 && two_ahead && (s & 3) == 1) issue_one<LT, PFX>(a, b, g, k0 + 2 * kBN, wave, lane, ks2, vs2, s >> 2);
       }
       bf16x8 pf[kRowBlocks][2];
 #pragma unroll
@@ -449,7 +448,7 @@ void prefill_kernel(PrefillArgs a) {
     }
     // Step 0 issues its prefetch after the MFMAs; the others issue it one instruction every
     // four QK MFMAs, or here when this wave's rows see no key of the tile.
-    if (two_ahead && (ST == 0 || !any_rb)) issue_tile<LT>(a, b, g, k0 + 2 * kBN, wave, lane, ks2, vs2);
+    if (two_ahead && (ST == 0 || !any_rb)) issue_tile<LT, PFX>(a, b, g, k0 + 2 * kBN, wave, lane, ks2, vs2);
     if (kt + 1 <= kt_hi) {
       // This lane's loads of tile kt+1 were issued one step ago; tile kt+2's may still be
       // in flight.  Every lane waits for its own loads before the barrier: other waves
@@ -541,7 +540,10 @@ hipError_t launch_prefill(int layer_type, const PrefillArgs& a, hipStream_t stre
   const dim3 rope_grid((unsigned)((chunks + 255) / 256));
   if (layer_type == kSliding) {
     hipLaunchKernelGGL(prefill_rope_kernel<kSliding>, rope_grid, dim3(256), 0, stream, a);
-    hipLaunchKernelGGL(prefill_kernel<kSliding>, dim3(blocks), dim3(kThreads), 0, stream, a);
+    if (a.start_pos > 0)
+      hipLaunchKernelGGL((prefill_kernel<kSliding, true>), dim3(blocks), dim3(kThreads), 0, stream, a);
+    else
+      hipLaunchKernelGGL((prefill_kernel<kSliding, false>), dim3(blocks), dim3(kThreads), 0, stream, a);
     if (a.start_pos > 0 && a.cache_k != nullptr) {
       const int kept = a.seq_len < kWindow ? a.seq_len : kWindow;
       const size_t n = (size_t)a.batch * kept * kKvHeads * 32;
@@ -549,7 +551,10 @@ hipError_t launch_prefill(int layer_type, const PrefillArgs& a, hipStream_t stre
     }
   } else {
     hipLaunchKernelGGL(prefill_rope_kernel<kFull>, rope_grid, dim3(256), 0, stream, a);
-    hipLaunchKernelGGL(prefill_kernel<kFull>, dim3(blocks), dim3(kThreads), 0, stream, a);
+    if (a.start_pos > 0)
+      hipLaunchKernelGGL((prefill_kernel<kFull, true>), dim3(blocks), dim3(kThreads), 0, stream, a);
+    else
+      hipLaunchKernelGGL((prefill_kernel<kFull, false>), dim3(blocks), dim3(kThreads), 0, stream, a);
   }
   return hipGetLastError();
 }
