@@ -13,7 +13,9 @@ Pages cited (titles as given by their addresses):
   [GGUF]  Sharp-Spark-X2.5-4B-GGUF on a 6 GB GPU (mpbf.cn/news/67460)
 
 Pinning status: every function is pinned by ``tests/test_oracle_*.py`` (closed forms,
-invariants, brute force, a library cross-check and the pages' KV-size figures).  What
+invariants, brute force, a library cross-check and the pages' KV-size figures); the
+8-bit cache (``kvq8``) by exact closed forms of the q8_0 rule, its error bound, and the
+bf16 append and decode it must agree with.  What
 no test can pin is numeric agreement with the real model's trained weights: none exist
 here, and the RoPE pairing convention (rotate-half) and the partial-rotary frequency
 denominator are readings of silent passages (both documented where used).
@@ -41,6 +43,13 @@ from .attention import (  # noqa: F401
     round_to_bf16_bits,
     softmax_scale,
     visibility,
+)
+from .kvq8 import (  # noqa: F401
+    Q8_BLOCK,
+    decode_q8,
+    kv_append_q8,
+    q8_dequantize,
+    q8_quantize,
 )
 from .footprint import (  # noqa: F401
     kv_bytes_full_layer_per_token,

@@ -293,10 +293,19 @@ def decode(q, gate, cache_k, cache_v, seq_lens, layer_type) -> np.ndarray:
     position L-1; the visible keys are positions 0..L-1 (full) or max(0, L-512)..L-1
     (sliding, read from ring slots p mod 512).  Returns float64 [B,16,256].
     """
+    return decode_rows(q, gate, lambda b, slots, g: bf16_to_f64(np.asarray(cache_k)[b, slots, g]),
+                       lambda b, slots, g: bf16_to_f64(np.asarray(cache_v)[b, slots, g]),
+                       np.asarray(cache_k).shape[2], seq_lens, layer_type)
+
+
+def decode_rows(q, gate, key_rows, value_rows, n_kv_heads: int, seq_lens, layer_type) -> np.ndarray:
+    """``decode`` over a cache given by accessors: key_rows(b, slots, g) and
+    value_rows(b, slots, g) return the float64 rows [len(slots), 256] of KV head g of
+    sequence b held in those slots."""
     th, rd, w = layer_params(layer_type)
     q = np.asarray(q)
     B, H, D = q.shape
-    Hk = np.asarray(cache_k).shape[2]
+    Hk = n_kv_heads
     scale = softmax_scale(D)
     out = np.zeros((B, H, D), dtype=np.float64)
     for b in range(B):
@@ -311,8 +320,8 @@ def decode(q, gate, cache_k, cache_v, seq_lens, layer_type) -> np.ndarray:
         qr = rope(bf16_to_f64(q[b])[None], [qp], th, rd)[0]          # [H, D]
         gb = bf16_to_f64(np.asarray(gate)[b])
         for g in range(Hk):                                          # one KV head at a time
-            kr = bf16_to_f64(np.asarray(cache_k)[b, slots, g])       # [n, D], already rotated
-            vb = bf16_to_f64(np.asarray(cache_v)[b, slots, g])
+            kr = key_rows(b, slots, g)                               # [n, D], already rotated
+            vb = value_rows(b, slots, g)
             for h in range(H):
                 if kv_head_of(h, H, Hk) == g:
                     out[b, h] = _attend(qr[h][None], kr, vb, vis, gb[h:h + 1], scale)[0]

@@ -481,6 +481,130 @@ def pin_footprint(att, fp):
                 assert abs(got - gb) <= 0.0101, f"KV table {ctx} {kind}: {got:.4f} vs {gb}"
 
 
+# --------------------------------------------------------------------------- 8-bit cache
+
+
+def pin_q8_closed_form(q8):
+    """Values that are whole multiples of a power-of-two step, with +-127 steps present in
+    every block, quantise to exactly those multiples: d = step, codes = the integers."""
+    rng = np.random.default_rng(51)
+    ints = rng.integers(-127, 128, size=(3, 256))
+    ints[:, ::32] = 127
+    ints[1, 1::32] = -127
+    steps = np.array([2.0 ** -(3 + (blk % 5)) for blk in range(8)])
+    x = (ints.reshape(3, 8, 32) * steps[None, :, None]).reshape(3, 256)
+    codes, scales = q8.q8_quantize(x)
+    assert codes.dtype == np.int8 and scales.dtype == np.float16
+    assert codes.shape == (3, 256) and scales.shape == (3, 8)
+    assert np.array_equal(codes.astype(np.int64), ints), "codes"
+    assert np.array_equal(scales.astype(np.float64), np.broadcast_to(steps, (3, 8))), "scales"
+    assert np.array_equal(q8.q8_dequantize(codes, scales), x), "read back"
+
+
+def pin_q8_zero_and_half_away(q8):
+    """An all-zero block stores scale 0 and codes 0; codes round half away from zero
+    (with d = 1: 2.5 -> 3, -2.5 -> -3, 0.5 -> 1, where nearest-even would give 2, -2, 0)."""
+    codes, scales = q8.q8_quantize(np.zeros((2, 64)))
+    assert not codes.any() and not scales.astype(np.float64).any()
+    assert not q8.q8_dequantize(codes, scales).any()
+    x = np.zeros(32)
+    x[:8] = [127.0, 2.5, -2.5, 0.5, -0.5, 3.5, -1.5, 126.5]
+    codes, scales = q8.q8_quantize(x)
+    assert float(scales[0]) == 1.0
+    assert codes[:8].tolist() == [127, 3, -3, 1, -1, 4, -2, 127], codes[:8].tolist()
+
+
+def pin_q8_error_bound(q8):
+    """Any correct q8_0 quantiser: codes within +-127, the largest magnitude of a nonzero
+    block at +-127, and every value read back within half a step (plus the fp16 rounding
+    of the step, up to 127 codes' worth) of the input; negating the input negates the codes."""
+    rng = np.random.default_rng(52)
+    x = np.concatenate([rng.standard_normal((40, 256)), rng.standard_cauchy((10, 256)),
+                        1e-3 * rng.standard_normal((10, 256))]).astype(np.float32)
+    codes, scales = q8.q8_quantize(x)
+    assert np.abs(codes.astype(np.int64)).max() <= 127
+    xb = np.abs(x.astype(np.float64)).reshape(60, 8, 32)
+    cb = codes.astype(np.int64).reshape(60, 8, 32)
+    top = np.take_along_axis(np.abs(cb), np.argmax(xb, axis=-1)[..., None], -1)[..., 0]
+    assert (top == 127).all()
+    d = xb.max(-1) / 127.0
+    d16 = scales.astype(np.float64)
+    err = np.abs(q8.q8_dequantize(codes, scales).reshape(60, 8, 32) - x.astype(np.float64).reshape(60, 8, 32))
+    bound = 0.5 * d * (1 + 1e-6) + 127 * np.abs(d16 - d) + 1e-12
+    assert (err <= bound[..., None]).all(), float((err - bound[..., None]).max())
+    nc, ns = q8.q8_quantize(-x)
+    assert np.array_equal(nc, -codes) and np.array_equal(ns, scales)
+
+
+def pin_q8_row_bytes(q8, fp):
+    """A K or V row of 256 values takes 256 code bytes and 8 fp16 scales: the q8_0 size
+    the KV footprint pin checks against the pages' table."""
+    codes, scales = q8.q8_quantize(np.ones((1, 256)))
+    assert codes.nbytes + scales.nbytes == fp.q8_0_bytes(256) == 272
+
+
+def _q8_cache(rng, B, cap):
+    kc = rng.integers(-127, 128, size=(B, cap, 4, 256)).astype(np.int8)
+    vc = rng.integers(-127, 128, size=(B, cap, 4, 256)).astype(np.int8)
+    ks = (rng.uniform(0.005, 0.03, size=(B, cap, 4, 8))).astype(np.float16)
+    vs = (rng.uniform(0.005, 0.03, size=(B, cap, 4, 8))).astype(np.float16)
+    return kc, ks, vc, vs
+
+
+def pin_kv_append_q8(att, q8):
+    """The 8-bit append writes what the bf16 append writes, read back within the q8_0
+    error bound, into the same slots (ring wrap included); untouched slots keep their
+    contents."""
+    rng = np.random.default_rng(53)
+    for lt, cap, pos, n in ((att.FULL, 64, [3, 20], 9), (att.SLIDING, 512, [505, 1000], 600)):
+        B = 2
+        k = rng.standard_normal((B, n, 4, 256)).astype(np.float32)
+        v = rng.standard_normal((B, n, 4, 256)).astype(np.float32)
+        kb, vb = att.round_to_bf16_bits(k), att.round_to_bf16_bits(v)
+        kc, ks, vc, vs = _q8_cache(rng, B, cap)
+        got = q8.kv_append_q8(kc, ks, vc, vs, kb, vb, np.array(pos), lt)
+        z = np.zeros((B, cap, 4, 256), np.uint16)
+        rk, rv = att.kv_append(z, z.copy(), kb, vb, np.array(pos), lt)
+        for b in range(B):
+            slots = sorted({att.cache_slot(p, lt) for p in range(pos[b], pos[b] + n)})
+            rest = np.setdiff1d(np.arange(cap), slots)
+            for name, codes, scales, old_c, old_s, ref in (("K", got[0], got[1], kc, ks, rk),
+                                                           ("V", got[2], got[3], vc, vs, rv)):
+                assert np.array_equal(codes[b, rest], old_c[b, rest]), f"{name} lt={lt}: untouched slots"
+                assert np.array_equal(scales[b, rest], old_s[b, rest]), f"{name} lt={lt}: untouched scales"
+                back = q8.q8_dequantize(codes[b, slots], scales[b, slots])
+                want = att.bf16_to_f64(ref[b, slots])
+                step = scales[b, slots].astype(np.float64).repeat(32, axis=-1)
+                # bf16 rounding of the reference (2^-9 relative) plus half a q8 step
+                assert (np.abs(back - want) <= 0.51 * step + 2.0 ** -8 * np.abs(want) + 1e-6).all(), \
+                    f"{name} lt={lt}: read-back beyond the q8_0 bound"
+        assert np.array_equal(got[2][0, att.cache_slot(pos[0] + n - 1, lt)], q8.q8_quantize(
+            att.bf16_to_f64(vb[0, n - 1]).astype(np.float32))[0]), "last value's codes"
+
+
+def pin_decode_q8(att, q8):
+    """Over a cache whose read-back values bf16 holds exactly (power-of-two steps, a
+    different one per block), the 8-bit decode equals the bf16 decode of those values."""
+    rng = np.random.default_rng(54)
+    for lt, cap, lens in ((att.FULL, 96, [1, 70, 96]), (att.SLIDING, 512, [3, 600, 1500])):
+        B = len(lens)
+        kc, _, vc, _ = _q8_cache(rng, B, cap)
+        ks = np.broadcast_to(np.array([2.0 ** -(4 + (j % 4)) for j in range(8)]), (B, cap, 4, 8)).astype(np.float16)
+        vs = np.broadcast_to(np.array([2.0 ** -(3 + (j % 3)) for j in range(8)]), (B, cap, 4, 8)).astype(np.float16)
+        q = att.round_to_bf16_bits(rng.standard_normal((B, 16, 256)))
+        g = att.round_to_bf16_bits(rng.standard_normal((B, 16)))
+        got = q8.decode_q8(q, g, kc, ks, vc, vs, np.array(lens), lt)
+        kbits = att.round_to_bf16_bits(q8.q8_dequantize(kc, ks))
+        vbits = att.round_to_bf16_bits(q8.q8_dequantize(vc, vs))
+        assert np.array_equal(att.bf16_to_f64(kbits), q8.q8_dequantize(kc, ks)), "values exact in bf16"
+        want = att.decode(q, g, kbits, vbits, np.array(lens), lt)
+        assert np.allclose(got, want, rtol=0, atol=1e-12), f"lt={lt}: {np.abs(got - want).max()}"
+
+
+Q8_PINS = [pin_q8_closed_form, pin_q8_zero_and_half_away, pin_q8_error_bound]
+Q8_ATT_PINS = [pin_kv_append_q8, pin_decode_q8]
+
+
 ALL_PINS = [
     pin_brute_force_tiny, pin_brute_force_real_heads, pin_window_covering_sequence_is_causal,
     pin_window_one_closed_form, pin_row_zero_closed_form, pin_constant_values,

@@ -56,3 +56,38 @@ def test_planted_mistake_is_caught(name):
             caught.append(pin.__name__)
             break
     assert caught, f"no pin fails for the planted mistake {name}"
+
+
+Q8_SRC = os.path.join(os.path.dirname(SRC), "kvq8.py")
+Q8_MUTANTS = {
+    "q8_divisor_128": ("amax / np.float32(127.0)", "amax / np.float32(128.0)"),
+    "q8_round_nearest_even": ("np.floor(np.abs(y64) + 0.5)", "np.round(np.abs(y64))"),
+    "q8_truncate": ("np.floor(np.abs(y64) + 0.5)", "np.floor(np.abs(y64))"),
+    "q8_scale_of_reversed_block": ("np.asarray(scales, dtype=np.float64)[..., None]",
+                                   "np.asarray(scales, dtype=np.float64)[..., ::-1, None]"),
+    "q8_key_not_rotated": ("kr = rope(bf16_to_f64(k[b]), p, th, rd).astype(np.float32)",
+                           "kr = bf16_to_f64(k[b]).astype(np.float32)"),
+    "q8_value_from_key": ("qv, dv = q8_quantize(bf16_to_f64(v[b]).astype(np.float32))",
+                          "qv, dv = q8_quantize(bf16_to_f64(k[b]).astype(np.float32))"),
+    "q8_decode_values_from_keys": ("lambda b, slots, g: q8_dequantize(vc[b, slots, g], vs[b, slots, g])",
+                                   "lambda b, slots, g: q8_dequantize(kc[b, slots, g], ks[b, slots, g])"),
+    "q8_append_slot_shift": ("s = cache_slot(int(p[t]), layer_type)", "s = cache_slot(int(p[t]) + 1, layer_type)"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(Q8_MUTANTS))
+def test_planted_q8_mistake_is_caught(name):
+    import oracle.attention as att
+    old, new = Q8_MUTANTS[name]
+    src = open(Q8_SRC).read()
+    assert src.count(old) == 1, f"mutation site must occur exactly once: {old!r}"
+    mod = types.ModuleType("oracle_q8_mutant")
+    exec(compile(src.replace(old, new), "oracle_q8_mutant", "exec"), mod.__dict__)
+    caught = []
+    for pin in P.Q8_PINS + P.Q8_ATT_PINS:
+        try:
+            pin(mod) if pin in P.Q8_PINS else pin(att, mod)
+        except (AssertionError, IndexError, ValueError):
+            caught.append(pin.__name__)
+            break
+    assert caught, f"no pin fails for the planted mistake {name}"

@@ -4,6 +4,7 @@ import pytest
 
 import oracle.attention as att
 import oracle.footprint as fp
+import oracle.kvq8 as q8
 import oracle_pins as P
 
 
@@ -14,3 +15,17 @@ def test_pin(pin):
 
 def test_footprint():
     P.pin_footprint(att, fp)
+
+
+@pytest.mark.parametrize("pin", P.Q8_PINS, ids=lambda f: f.__name__)
+def test_q8_pin(pin):
+    pin(q8)
+
+
+@pytest.mark.parametrize("pin", P.Q8_ATT_PINS, ids=lambda f: f.__name__)
+def test_q8_att_pin(pin):
+    pin(att, q8)
+
+
+def test_q8_row_bytes():
+    P.pin_q8_row_bytes(q8, fp)
