@@ -33,6 +33,11 @@ class KvCacheDesc(ctypes.Structure):
                 ("batch", ctypes.c_int32), ("capacity", ctypes.c_int32)]
 
 
+class KvCacheQ8Desc(ctypes.Structure):
+    _fields_ = [("k", ctypes.c_void_p), ("k_scale", ctypes.c_void_p), ("v", ctypes.c_void_p),
+                ("v_scale", ctypes.c_void_p), ("batch", ctypes.c_int32), ("capacity", ctypes.c_int32)]
+
+
 def _load():
     # torch is imported first on purpose: it ships its own HIP runtime, and the library's
     # dependency on libamdhip64.so.7 must resolve to that already-loaded copy.  Loading
@@ -57,6 +62,11 @@ def _load():
     lib.spark_attn_decode_workspace_bytes.restype = sz
     lib.spark_attn_decode.argtypes = [i32, i32, vp, vp, cache_p, vp, i32, i32, vp, sz, vp, vp]
     lib.spark_attn_decode.restype = i32
+    q8_p = ctypes.POINTER(KvCacheQ8Desc)
+    lib.spark_kv_append_q8.argtypes = [i32, i32, i32, vp, vp, vp, q8_p, vp]
+    lib.spark_kv_append_q8.restype = i32
+    lib.spark_attn_decode_q8.argtypes = [i32, i32, vp, vp, q8_p, vp, i32, i32, vp, sz, vp, vp]
+    lib.spark_attn_decode_q8.restype = i32
     lib.spark_status_string.argtypes = [i32]
     lib.spark_status_string.restype = ctypes.c_char_p
     lib.spark_abi_version.argtypes = []
@@ -68,7 +78,8 @@ _lib = _load()
 
 LIBRARY_PATH = _LIB_PATH
 EXPORTED = ("spark_attn_prefill_workspace_bytes", "spark_attn_prefill", "spark_kv_append", "spark_attn_decode_workspace_bytes",
-            "spark_attn_decode", "spark_status_string", "spark_abi_version")
+            "spark_attn_decode", "spark_kv_append_q8", "spark_attn_decode_q8", "spark_status_string",
+            "spark_abi_version")
 
 
 def abi_version() -> int:
@@ -133,6 +144,37 @@ class KVCache:
 
     def desc(self) -> KvCacheDesc:
         return KvCacheDesc(self.k.data_ptr(), self.v.data_ptr(), self.batch, self.capacity)
+
+
+class KVCacheQ8:
+    """One layer's 8-bit KV cache (q8_0 blocks of 32 along head_dim): int8 codes
+    [batch, capacity, 4, 256] and fp16 scales [batch, capacity, 4, 8] for K (post-RoPE)
+    and for V.  Capacity rules as for KVCache."""
+
+    def __init__(self, layer_type: int, batch: int, capacity: int | None = None, device="cuda",
+                 k=None, k_scale=None, v=None, v_scale=None):
+        torch = _torch()
+        if layer_type == SLIDING:
+            capacity = WINDOW if capacity is None else capacity
+        elif capacity is None:
+            raise ValueError("a full-layer cache needs a capacity")
+        self.layer_type = int(layer_type)
+        self.batch = int(batch)
+        self.capacity = int(capacity)
+        shape = (self.batch, self.capacity, N_KV_HEADS, HEAD_DIM)
+        sshape = (self.batch, self.capacity, N_KV_HEADS, HEAD_DIM // 32)
+        self.k = torch.zeros(shape, dtype=torch.int8, device=device) if k is None else k
+        self.v = torch.zeros(shape, dtype=torch.int8, device=device) if v is None else v
+        self.k_scale = torch.zeros(sshape, dtype=torch.float16, device=device) if k_scale is None else k_scale
+        self.v_scale = torch.zeros(sshape, dtype=torch.float16, device=device) if v_scale is None else v_scale
+        _check(self.k, "cache.k", shape, torch.int8)
+        _check(self.v, "cache.v", shape, torch.int8)
+        _check(self.k_scale, "cache.k_scale", sshape, torch.float16)
+        _check(self.v_scale, "cache.v_scale", sshape, torch.float16)
+
+    def desc(self) -> KvCacheQ8Desc:
+        return KvCacheQ8Desc(self.k.data_ptr(), self.k_scale.data_ptr(), self.v.data_ptr(),
+                             self.v_scale.data_ptr(), self.batch, self.capacity)
 
 
 def prefill_workspace_bytes(layer_type: int, batch: int, seq_len: int) -> int:
@@ -214,6 +256,46 @@ def decode(layer_type: int, q, gate, cache: KVCache, seq_lens, max_seq_len: int,
                                 int(workspace.numel()), _ptr(out), _stream(stream))
     if st:
         raise SparkError(st, "spark_attn_decode")
+    return out
+
+
+def kv_append_q8(layer_type: int, k, v, pos, cache: KVCacheQ8, stream=None):
+    """spark_kv_append_q8: k/v [B,n_new,4,256] bf16 (k pre-RoPE), pos device int32 [B]."""
+    torch = _torch()
+    B, n = int(k.shape[0]), int(k.shape[1])
+    _check(k, "k", (B, n, N_KV_HEADS, HEAD_DIM), torch.bfloat16)
+    _check(v, "v", (B, n, N_KV_HEADS, HEAD_DIM), torch.bfloat16)
+    _check(pos, "pos", (B,), torch.int32)
+    if cache.layer_type != layer_type:
+        raise ValueError("cache layer type differs from the call's")
+    st = _lib.spark_kv_append_q8(int(layer_type), B, n, _ptr(k), _ptr(v), _ptr(pos),
+                                 ctypes.pointer(cache.desc()), _stream(stream))
+    if st:
+        raise SparkError(st, "spark_kv_append_q8")
+
+
+def decode_q8(layer_type: int, q, gate, cache: KVCacheQ8, seq_lens, max_seq_len: int, out=None,
+              workspace=None, num_parts: int = 0, stream=None):
+    """spark_attn_decode_q8: decode against an 8-bit cache; arguments as for decode."""
+    torch = _torch()
+    B = int(q.shape[0])
+    _check(q, "q", (B, N_Q_HEADS, HEAD_DIM), torch.bfloat16)
+    _check(gate, "gate", (B, N_Q_HEADS), torch.bfloat16)
+    _check(seq_lens, "seq_lens", (B,), torch.int32)
+    if cache.layer_type != layer_type:
+        raise ValueError("cache layer type differs from the call's")
+    need = decode_workspace_bytes(layer_type, B, max_seq_len, num_parts)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    _check(workspace, "workspace", None, torch.uint8)
+    if out is None:
+        out = torch.empty_like(q)
+    _check(out, "out", tuple(q.shape), torch.bfloat16)
+    st = _lib.spark_attn_decode_q8(int(layer_type), B, _ptr(q), _ptr(gate), ctypes.pointer(cache.desc()),
+                                   _ptr(seq_lens), int(max_seq_len), int(num_parts), _ptr(workspace),
+                                   int(workspace.numel()), _ptr(out), _stream(stream))
+    if st:
+        raise SparkError(st, "spark_attn_decode_q8")
     return out
 
 

@@ -1,5 +1,5 @@
 // extern "C" entry points declared in include/spark_attn.h: host-side argument checks,
-// then the launches (prefill two, append one, decode three) on the caller's stream.  Every check
+// then the launches (prefill two or three, append one, decode two) on the caller's stream.  Every check
 // runs before any HIP call, so a rejected call enqueues nothing and touches no device.
 #include "spark_attn.h"
 #include "spark_device.hpp"
@@ -23,7 +23,49 @@ spark_status check_cache(int32_t lt, const spark_kv_cache* c, int32_t batch) {
   return SPARK_OK;
 }
 
+spark_status check_cache_q8(int32_t lt, const spark_kv_cache_q8* c, int32_t batch) {
+  if (!c || !c->k || !c->v || !c->k_scale || !c->v_scale) return SPARK_ERR_INVALID_ARG;
+  if (!aligned16(c->k) || !aligned16(c->v) || !aligned16(c->k_scale) || !aligned16(c->v_scale))
+    return SPARK_ERR_INVALID_ARG;
+  if (c->batch != batch || c->capacity < 1) return SPARK_ERR_INVALID_ARG;
+  if (lt == SPARK_LAYER_SLIDING && c->capacity != SPARK_WINDOW) return SPARK_ERR_INVALID_ARG;
+  return SPARK_OK;
+}
+
 spark_status from_hip(hipError_t e) { return e == hipSuccess ? SPARK_OK : SPARK_ERR_HIP; }
+
+// Checks shared by spark_attn_decode and spark_attn_decode_q8 (everything but the cache).
+spark_status check_decode(int32_t layer_type, int32_t batch, const void* q, const void* gate_logits,
+                          const int32_t* seq_lens, int32_t max_seq_len, int32_t num_parts,
+                          const void* workspace, const void* out) {
+  if (!valid_type(layer_type)) return SPARK_ERR_INVALID_ARG;
+  if (batch < 1 || batch > kMaxBatch || max_seq_len < 1 || max_seq_len > kMaxSeq) return SPARK_ERR_INVALID_ARG;
+  if (num_parts < 0 || num_parts > kMaxParts) return SPARK_ERR_INVALID_ARG;
+  if (!q || !gate_logits || !seq_lens || !out || !workspace) return SPARK_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(out) || !aligned2(gate_logits) ||
+      (reinterpret_cast<uintptr_t>(seq_lens) & 3u) || (reinterpret_cast<uintptr_t>(workspace) & 255u))
+    return SPARK_ERR_INVALID_ARG;
+  return SPARK_OK;
+}
+
+// Decode arguments after the checks: the workspace regions of the plan.
+spark::DecodeArgs decode_args(const spark::DecodePlan& plan, int32_t batch, int32_t cap, const void* q,
+                              const void* gate_logits, const int32_t* seq_lens, void* workspace,
+                              void* out) {
+  char* ws = static_cast<char*>(workspace);
+  spark::DecodeArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.gate = static_cast<const uint16_t*>(gate_logits);
+  a.seq_lens = seq_lens;
+  a.ws_range = reinterpret_cast<int2*>(ws + plan.range_offset);
+  a.ws_o = reinterpret_cast<float*>(ws + plan.o_offset);
+  a.ws_ml = reinterpret_cast<float*>(ws + plan.ml_offset);
+  a.out = static_cast<uint16_t*>(out);
+  a.batch = batch;
+  a.cache_cap = cap;
+  a.nparts = plan.nparts;
+  return a;
+}
 
 }  // namespace
 
@@ -127,35 +169,64 @@ spark_status spark_attn_decode(int32_t layer_type, int32_t batch, const void* q,
                                const int32_t* seq_lens, int32_t max_seq_len,
                                int32_t num_parts, void* workspace,
                                size_t workspace_bytes, void* out, void* stream) {
-  if (!valid_type(layer_type)) return SPARK_ERR_INVALID_ARG;
-  if (batch < 1 || batch > kMaxBatch || max_seq_len < 1 || max_seq_len > kMaxSeq) return SPARK_ERR_INVALID_ARG;
-  if (num_parts < 0 || num_parts > kMaxParts) return SPARK_ERR_INVALID_ARG;
-  if (!q || !gate_logits || !seq_lens || !out || !workspace) return SPARK_ERR_INVALID_ARG;
-  if (!aligned16(q) || !aligned16(out) || !aligned2(gate_logits) ||
-      (reinterpret_cast<uintptr_t>(seq_lens) & 3u) || (reinterpret_cast<uintptr_t>(workspace) & 255u))
-    return SPARK_ERR_INVALID_ARG;
-  const spark_status cs = check_cache(layer_type, cache, batch);
-  if (cs != SPARK_OK) return cs;
+  spark_status st = check_decode(layer_type, batch, q, gate_logits, seq_lens, max_seq_len, num_parts,
+                                 workspace, out);
+  if (st != SPARK_OK) return st;
+  st = check_cache(layer_type, cache, batch);
+  if (st != SPARK_OK) return st;
   if (layer_type == SPARK_LAYER_FULL && max_seq_len > cache->capacity) return SPARK_ERR_INVALID_ARG;
   // Planned on max_seq_len (not the capacity), exactly as the workspace query plans it.
   const spark::DecodePlan plan = spark::plan_decode(layer_type, batch, max_seq_len, num_parts);
   if (workspace_bytes < plan.total_bytes) return SPARK_ERR_WORKSPACE;
-
-  char* ws = static_cast<char*>(workspace);
-  spark::DecodeArgs a{};
-  a.q = static_cast<const uint16_t*>(q);
-  a.gate = static_cast<const uint16_t*>(gate_logits);
+  spark::DecodeArgs a = decode_args(plan, batch, cache->capacity, q, gate_logits, seq_lens, workspace, out);
   a.cache_k = static_cast<const uint16_t*>(cache->k);
   a.cache_v = static_cast<const uint16_t*>(cache->v);
-  a.seq_lens = seq_lens;
-  a.ws_range = reinterpret_cast<int2*>(ws + plan.range_offset);
-  a.ws_o = reinterpret_cast<float*>(ws + plan.o_offset);
-  a.ws_ml = reinterpret_cast<float*>(ws + plan.ml_offset);
-  a.out = static_cast<uint16_t*>(out);
-  a.batch = batch;
-  a.cache_cap = cache->capacity;
-  a.nparts = plan.nparts;
   return from_hip(spark::launch_decode(layer_type, a, static_cast<hipStream_t>(stream)));
+}
+
+spark_status spark_kv_append_q8(int32_t layer_type, int32_t batch, int32_t n_new,
+                                const void* k, const void* v, const int32_t* pos,
+                                const spark_kv_cache_q8* cache, void* stream) {
+  if (!valid_type(layer_type)) return SPARK_ERR_INVALID_ARG;
+  if (batch < 1 || batch > kMaxBatch || n_new < 1 || n_new > kMaxSeq) return SPARK_ERR_INVALID_ARG;
+  if (!k || !v || !pos) return SPARK_ERR_INVALID_ARG;
+  if (!aligned16(k) || !aligned16(v) || (reinterpret_cast<uintptr_t>(pos) & 3u)) return SPARK_ERR_INVALID_ARG;
+  const spark_status cs = check_cache_q8(layer_type, cache, batch);
+  if (cs != SPARK_OK) return cs;
+
+  spark::AppendQ8Args a{};
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.pos = pos;
+  a.k_codes = static_cast<int8_t*>(cache->k);
+  a.k_scales = static_cast<uint16_t*>(cache->k_scale);
+  a.v_codes = static_cast<int8_t*>(cache->v);
+  a.v_scales = static_cast<uint16_t*>(cache->v_scale);
+  a.batch = batch;
+  a.n_new = n_new;
+  a.cache_cap = cache->capacity;
+  return from_hip(spark::launch_append_q8(layer_type, a, static_cast<hipStream_t>(stream)));
+}
+
+spark_status spark_attn_decode_q8(int32_t layer_type, int32_t batch, const void* q,
+                                  const void* gate_logits, const spark_kv_cache_q8* cache,
+                                  const int32_t* seq_lens, int32_t max_seq_len,
+                                  int32_t num_parts, void* workspace,
+                                  size_t workspace_bytes, void* out, void* stream) {
+  spark_status st = check_decode(layer_type, batch, q, gate_logits, seq_lens, max_seq_len, num_parts,
+                                 workspace, out);
+  if (st != SPARK_OK) return st;
+  st = check_cache_q8(layer_type, cache, batch);
+  if (st != SPARK_OK) return st;
+  if (layer_type == SPARK_LAYER_FULL && max_seq_len > cache->capacity) return SPARK_ERR_INVALID_ARG;
+  const spark::DecodePlan plan = spark::plan_decode(layer_type, batch, max_seq_len, num_parts);
+  if (workspace_bytes < plan.total_bytes) return SPARK_ERR_WORKSPACE;
+  spark::DecodeArgs a = decode_args(plan, batch, cache->capacity, q, gate_logits, seq_lens, workspace, out);
+  a.k_codes = static_cast<const int8_t*>(cache->k);
+  a.k_scales = static_cast<const uint16_t*>(cache->k_scale);
+  a.v_codes = static_cast<const int8_t*>(cache->v);
+  a.v_scales = static_cast<const uint16_t*>(cache->v_scale);
+  return from_hip(spark::launch_decode_q8(layer_type, a, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

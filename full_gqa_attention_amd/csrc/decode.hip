@@ -25,6 +25,12 @@
 //   * merge: per (sequence, query head), the partials of the partitions that touched the
 //     sequence are combined with log-sum-exp weights and the sigmoid head gate is applied.
 // Sliding layers read the 512-slot ring; full layers the contiguous cache.
+//
+// The 8-bit cache (q8_0 blocks of 32 along head_dim, Sharp-Spark-X2.5-4B-GGUF guide,
+// section 四) runs the same kernels with Q8 = true: each 32-dim MFMA step of S = Q K^T is
+// exactly one quantisation block, so the K codes enter the MFMA as bf16 integers (exact,
+// |code| <= 127) and the step's result is scaled by that key's block scale in fp32; V
+// codes are read back as code * scale on the VALU.
 #include "spark_device.hpp"
 #include "spark_launch.hpp"
 
@@ -56,9 +62,24 @@ __device__ __forceinline__ int part_of(int x, int C, int P) {
   return (int)((((long long)(x + 1) * P) + C - 1) / C) - 1;
 }
 
+__device__ __forceinline__ float half_to_f32(uint32_t bits16) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);
+}
+
+// Eight int8 codes (two dwords) as eight exact bf16 values.
+__device__ __forceinline__ bf16x8 codes_to_bf16(u32x2 x) {
+  u32x4 r;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const uint32_t d = x[w >> 1] >> (16 * (w & 1));
+    r[w] = pack_bf16x2((float)(int8_t)(d & 0xff), (float)(int8_t)((d >> 8) & 0xff));
+  }
+  return as_bf16x8(r);
+}
+
 // Online-softmax attention of the 4 query heads of KV head g of sequence b over keys
 // [ks, ke) of its cache; writes the partial result to slot `slot`.
-template <int LT>
+template <int LT, bool Q8>
 __device__ __forceinline__ void attend_segment(const DecodeArgs& a, int b, int L, int ks, int ke,
                                                int slot, int g, int lane, const double* s_inv,
                                                float (*s_p)[kChunk][4], float (*s_alpha)[4]) {
@@ -102,26 +123,54 @@ __device__ __forceinline__ void attend_segment(const DecodeArgs& a, int b, int L
     for (int e = 0; e < 8; ++e) acc[h][e] = 0.0f;
   }
 
+  // 8-bit cache: codes at the same element offsets (one byte each); scales [slot][4][8].
+  const int8_t* kbase8 = a.k_codes + seq_base;
+  const int8_t* vbase8 = a.v_codes + seq_base;
+  const size_t sc_base = ((size_t)b * a.cache_cap * kKvHeads + g) * 8;
+
   for (int c0 = ks; c0 < ke; c0 += kChunk) {
     u32x4 kr[2][8];
+    u32x2 kr8[2][8];
+    u32x4 ksc[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       const int key = c0 + 16 * kb + hrow;
       const bool ok = key < ke;
-      const uint16_t* src = kbase + (size_t)(ok ? key : ks) * kSlot + 8 * kq;
+      const size_t row = (size_t)(ok ? key : ks);
+      if constexpr (Q8) {
+        const int8_t* src = kbase8 + row * kSlot + 8 * kq;
 #pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        const u32x4 x = ld_global16(src + 32 * s);
-        kr[kb][s] = ok ? x : u32x4{0, 0, 0, 0};
+        for (int s = 0; s < 8; ++s) {
+          const u32x2 x = *reinterpret_cast<const u32x2*>(src + 32 * s);
+          kr8[kb][s] = ok ? x : u32x2{0, 0};
+        }
+        ksc[kb] = ld_global16(a.k_scales + sc_base + row * (kKvHeads * 8));
+      } else {
+        const uint16_t* src = kbase + row * kSlot + 8 * kq;
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+          const u32x4 x = ld_global16(src + 32 * s);
+          kr[kb][s] = ok ? x : u32x4{0, 0, 0, 0};
+        }
       }
     }
     u32x4 vr[16];
+    u32x2 vr8[16];
+    float vsc[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int key = c0 + 2 * i + vpar;
       const bool ok = key < ke;
-      const u32x4 x = ld_global16(vbase + (size_t)(ok ? key : ks) * kSlot + vdim);
-      vr[i] = ok ? x : u32x4{0, 0, 0, 0};
+      const size_t row = (size_t)(ok ? key : ks);
+      if constexpr (Q8) {
+        const u32x2 x = *reinterpret_cast<const u32x2*>(vbase8 + row * kSlot + vdim);
+        vr8[i] = ok ? x : u32x2{0, 0};
+        const float d = half_to_f32(a.v_scales[sc_base + row * (kKvHeads * 8) + (vdim >> 5)]);
+        vsc[i] = ok ? d : 0.0f;
+      } else {
+        const u32x4 x = ld_global16(vbase + row * kSlot + vdim);
+        vr[i] = ok ? x : u32x4{0, 0, 0, 0};
+      }
     }
 
     // Scores: lanes 0..15 hold heads 0..3 (element v) for key c0 + 16kb + lane.
@@ -129,8 +178,19 @@ __device__ __forceinline__ void attend_segment(const DecodeArgs& a, int b, int L
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       f32x4 sc = f32x4{0, 0, 0, 0};
+      if constexpr (Q8) {
+        // Step s is block s of the key row; lanes 0..15 hold key hrow, whose scales
+        // ksc[kb] holds (eight fp16).
 #pragma unroll
-      for (int s = 0; s < 8; ++s) sc = mfma_16x16x32(qa[s], as_bf16x8(kr[kb][s]), sc);
+        for (int s = 0; s < 8; ++s) {
+          const f32x4 part = mfma_16x16x32(qa[s], codes_to_bf16(kr8[kb][s]), f32x4{0, 0, 0, 0});
+          const float d = half_to_f32(ksc[kb][s >> 1] >> (16 * (s & 1)));
+          sc += d * part;
+        }
+      } else {
+#pragma unroll
+        for (int s = 0; s < 8; ++s) sc = mfma_16x16x32(qa[s], as_bf16x8(kr[kb][s]), sc);
+      }
       const bool ok = c0 + 16 * kb + hrow < ke;
 #pragma unroll
       for (int v = 0; v < 4; ++v) t[kb][v] = ok ? sc[v] * kScoreScaleLog2 : -INFINITY;
@@ -168,12 +228,18 @@ __device__ __forceinline__ void attend_segment(const DecodeArgs& a, int b, int L
       for (int e = 0; e < 8; ++e) acc[h][e] *= al[h];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const f32x4 pp = *reinterpret_cast<const f32x4*>(&s_p[g][2 * i + vpar][0]);
+      f32x4 pp = *reinterpret_cast<const f32x4*>(&s_p[g][2 * i + vpar][0]);
       float x[8];
+      if constexpr (Q8) {
+        pp *= vsc[i];                          // value = code * scale: fold the scale into P
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        x[2 * w] = bf16_lo(vr[i][w]);
-        x[2 * w + 1] = bf16_hi(vr[i][w]);
+        for (int e = 0; e < 8; ++e) x[e] = (float)(int8_t)((vr8[i][e >> 2] >> (8 * (e & 3))) & 0xff);
+      } else {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          x[2 * w] = bf16_lo(vr[i][w]);
+          x[2 * w + 1] = bf16_hi(vr[i][w]);
+        }
       }
 #pragma unroll
       for (int h = 0; h < 4; ++h)
@@ -207,7 +273,7 @@ __device__ __forceinline__ void attend_segment(const DecodeArgs& a, int b, int L
   }
 }
 
-template <int LT>
+template <int LT, bool Q8>
 __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
   using T = LayerTraits<LT>;
   __shared__ double s_inv[T::kRot / 2];
@@ -270,7 +336,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
     if (cn > lo && cn > cb) {
       const int ks = (max(lo, cb) - cb) * kChunk;
       const int ke = min((min(hi, cn) - cb) * kChunk, n);
-      attend_segment<LT>(a, b, L, ks, ke, w + b, g, lane, s_inv, s_p, s_alpha);
+      attend_segment<LT, Q8>(a, b, L, ks, ke, w + b, g, lane, s_inv, s_p, s_alpha);
     }
     if (cn >= hi || b + 1 >= a.batch) break;
     ++b;
@@ -362,16 +428,23 @@ DecodePlan plan_decode(int layer_type, int batch, int max_seq_len, int nparts) {
   return p;
 }
 
-hipError_t launch_decode(int layer_type, const DecodeArgs& a, hipStream_t stream) {
+template <bool Q8>
+hipError_t launch_decode_impl(int layer_type, const DecodeArgs& a, hipStream_t stream) {
   const dim3 grid_reduce(a.batch * kQHeads);
-  if (layer_type == kSliding) {
-    hipLaunchKernelGGL(decode_split_kernel<kSliding>, dim3(a.nparts), dim3(kThreads), 0, stream, a);
-    hipLaunchKernelGGL(decode_reduce_kernel, grid_reduce, dim3(64 * kReduceWaves), 0, stream, a);
-  } else {
-    hipLaunchKernelGGL(decode_split_kernel<kFull>, dim3(a.nparts), dim3(kThreads), 0, stream, a);
-    hipLaunchKernelGGL(decode_reduce_kernel, grid_reduce, dim3(64 * kReduceWaves), 0, stream, a);
-  }
+  if (layer_type == kSliding)
+    hipLaunchKernelGGL((decode_split_kernel<kSliding, Q8>), dim3(a.nparts), dim3(kThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL((decode_split_kernel<kFull, Q8>), dim3(a.nparts), dim3(kThreads), 0, stream, a);
+  hipLaunchKernelGGL(decode_reduce_kernel, grid_reduce, dim3(64 * kReduceWaves), 0, stream, a);
   return hipGetLastError();
+}
+
+hipError_t launch_decode(int layer_type, const DecodeArgs& a, hipStream_t stream) {
+  return launch_decode_impl<false>(layer_type, a, stream);
+}
+
+hipError_t launch_decode_q8(int layer_type, const DecodeArgs& a, hipStream_t stream) {
+  return launch_decode_impl<true>(layer_type, a, stream);
 }
 
 }  // namespace spark

@@ -34,11 +34,30 @@ struct AppendArgs {
   int cache_cap;
 };
 
+// 8-bit cache (q8_0 blocks of 32 along head_dim): codes [B, cap, 4, 256] int8, scales
+// [B, cap, 4, 8] fp16, for K and for V.
+struct AppendQ8Args {
+  const uint16_t* k;      // [B, n_new, 4, 256] bf16
+  const uint16_t* v;
+  const int32_t* pos;     // [B]
+  int8_t* k_codes;
+  uint16_t* k_scales;
+  int8_t* v_codes;
+  uint16_t* v_scales;
+  int batch;
+  int n_new;
+  int cache_cap;
+};
+
 struct DecodeArgs {
   const uint16_t* q;      // [B, 16, 256]
   const uint16_t* gate;   // [B, 16]
-  const uint16_t* cache_k;
+  const uint16_t* cache_k;  // bf16 cache (decode)
   const uint16_t* cache_v;
+  const int8_t* k_codes;    // 8-bit cache (decode_q8)
+  const uint16_t* k_scales;
+  const int8_t* v_codes;
+  const uint16_t* v_scales;
   const int32_t* seq_lens;
   int2* ws_range;         // [B] first and last partition touching each sequence
   float* ws_o;            // [P + B, 16, 256] partial results, slot = partition + sequence
@@ -52,6 +71,8 @@ struct DecodeArgs {
 hipError_t launch_prefill(int layer_type, const PrefillArgs& a, hipStream_t stream);
 hipError_t launch_append(int layer_type, const AppendArgs& a, hipStream_t stream);
 hipError_t launch_decode(int layer_type, const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_append_q8(int layer_type, const AppendQ8Args& a, hipStream_t stream);
+hipError_t launch_decode_q8(int layer_type, const DecodeArgs& a, hipStream_t stream);
 
 int prefill_block_rows();
 size_t prefill_workspace_bytes(int batch, int seq_len);

@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define SPARK_ATTN_ABI_VERSION 4
+#define SPARK_ATTN_ABI_VERSION 5
 
 enum { SPARK_Q_HEADS = 16, SPARK_KV_HEADS = 4, SPARK_HEAD_DIM = 256, SPARK_WINDOW = 512 };
 
@@ -165,6 +165,49 @@ spark_status spark_attn_decode(int32_t layer_type, int32_t batch, const void* q,
                                const int32_t* seq_lens, int32_t max_seq_len,
                                int32_t num_parts, void* workspace,
                                size_t workspace_bytes, void* out, void* stream);
+
+/*
+ * 8-bit KV cache of one layer: the q8_0 format the Sharp-Spark-X2.5-4B-GGUF guide
+ * (mpbf.cn/news/67460, section 四) enables with --cache-type-k/v q8_0, 36 -> 19 KB per
+ * token over the 9 full layers.  Each K or V row of 256 values is 8 blocks of 32; a block
+ * stores one scale d = max|x| / 127 (fp16) and 32 int8 codes round(x / d), rounded half
+ * away from zero (all 0 when d = 0); the value reads back as code * d.  Decisions are
+ * taken in fp32 (d, 1/d and x * (1/d)), and d is rounded to fp16 to nearest even.
+ *   k, v               int8 codes [batch, capacity, 4, 256], 16-byte aligned
+ *   k_scale, v_scale   fp16 scales [batch, capacity, 4, 8], 16-byte aligned
+ * Keys are quantised after RoPE; slots and capacity rules are those of spark_kv_cache.
+ * Per token and KV head: 256 + 16 bytes for K and as much for V (bf16: 512 + 512).
+ */
+typedef struct spark_kv_cache_q8 {
+  void* k;
+  void* k_scale;
+  void* v;
+  void* v_scale;
+  int32_t batch;
+  int32_t capacity;
+} spark_kv_cache_q8;
+
+/*
+ * spark_kv_append into an 8-bit cache: token t of sequence b is rotated at position
+ * pos[b] + t (in fp32, never rounded to bf16), and its key and value are quantised as
+ * above into the same slot spark_kv_append would use.  Same arguments, limits and errors
+ * as spark_kv_append.
+ */
+spark_status spark_kv_append_q8(int32_t layer_type, int32_t batch, int32_t n_new,
+                                const void* k, const void* v, const int32_t* pos,
+                                const spark_kv_cache_q8* cache, void* stream);
+
+/*
+ * spark_attn_decode against an 8-bit cache: keys and values read back as code * scale.
+ * Same arguments, limits, workspace (size from spark_attn_decode_workspace_bytes) and
+ * errors as spark_attn_decode; the two launches stream 272 + 272 bytes per key and KV
+ * head instead of 512 + 512.
+ */
+spark_status spark_attn_decode_q8(int32_t layer_type, int32_t batch, const void* q,
+                                  const void* gate_logits, const spark_kv_cache_q8* cache,
+                                  const int32_t* seq_lens, int32_t max_seq_len,
+                                  int32_t num_parts, void* workspace,
+                                  size_t workspace_bytes, void* out, void* stream);
 
 /* Static description of a status code; never NULL. */
 const char* spark_status_string(int32_t status);

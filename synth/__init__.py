@@ -115,3 +115,41 @@ def decode_inputs(seed: int, batch: int, capacity: int, fill_lens=None) -> dict:
         n = capacity if fill_lens is None else min(int(fill_lens[b]), capacity)
         ck[b, :n], cv[b, :n] = cache_rows(seed, b, n)
     return {"q": q, "gate": gate, "cache_k": ck, "cache_v": cv}
+
+
+def int8_codes(seed: int, tensor_index: int, shape) -> np.ndarray:
+    """Uniform int8 values in [-127, 127] of ``shape`` (blocked streams as above)."""
+    shape = tuple(int(s) for s in shape)
+    n = int(np.prod(shape)) if shape else 1
+    out = np.empty(n, dtype=np.int8)
+    nblk = (n + BLOCK - 1) // BLOCK
+
+    def fill(i: int) -> None:
+        lo = i * BLOCK
+        hi = min(n, lo + BLOCK)
+        ss = np.random.SeedSequence(seed, spawn_key=(tensor_index, i))
+        out[lo:hi] = np.random.default_rng(ss).integers(-127, 128, hi - lo, dtype=np.int16).astype(np.int8)
+
+    if nblk <= 1:
+        for i in range(nblk):
+            fill(i)
+    else:
+        with ThreadPoolExecutor(_threads()) as ex:
+            list(ex.map(fill, range(nblk)))
+    return out.reshape(shape)
+
+
+def fp16_scales(seed: int, tensor_index: int, shape, lo: float = 0.005, hi: float = 0.03) -> np.ndarray:
+    """Uniform fp16 values in [lo, hi) of ``shape`` (one stream; scales are small)."""
+    rng = np.random.default_rng(np.random.SeedSequence(seed, spawn_key=(tensor_index, 0)))
+    return rng.uniform(lo, hi, size=tuple(int(s) for s in shape)).astype(np.float16)
+
+
+def q8_cache_rows(seed: int, b: int, n: int) -> tuple:
+    """8-bit cache rows of sequence ``b``: (K codes, K scales, V codes, V scales), codes
+    [n,4,256] int8 and scales [n,4,8] fp16 (a q8_0 step of 0.005-0.03 spans about the
+    range of N(0,1) values)."""
+    return (int8_codes(seed, 100 + 4 * b, (n, N_KV_HEADS, HEAD_DIM)),
+            fp16_scales(seed, 101 + 4 * b, (n, N_KV_HEADS, HEAD_DIM // 32)),
+            int8_codes(seed, 102 + 4 * b, (n, N_KV_HEADS, HEAD_DIM)),
+            fp16_scales(seed, 103 + 4 * b, (n, N_KV_HEADS, HEAD_DIM // 32)))

@@ -30,7 +30,7 @@ def test_exports_every_declared_function():
 
 
 def test_version_and_status_strings():
-    assert fga.abi_version() == 4
+    assert fga.abi_version() == 5
     assert fga.status_string(0) == "ok"
     assert fga.status_string(3) == "workspace too small"
     assert fga.status_string(99) == "unknown status"
@@ -112,3 +112,32 @@ def test_decode_rejects():
     assert f(1, 1, FAKE, FAKE, _cache(cap=64), FAKE, 64, 2, FAKE, 16, FAKE, None) == 3    # workspace
     assert f(1, 1, FAKE, FAKE, _cache(cap=64), FAKE, 64, 0, MISALIGNED, big, FAKE, None) == 1
     assert f(0, 1, FAKE, FAKE, _cache(cap=1024), FAKE, 64, 0, FAKE, big, FAKE, None) == 1
+
+
+def _cache_q8(k=FAKE, ks=FAKE, v=FAKE, vs=FAKE, batch=1, cap=512):
+    val = lambda p: p.value if p else None
+    return ctypes.pointer(fga.KvCacheQ8Desc(val(k), val(ks), val(v), val(vs), batch, cap))
+
+
+def test_append_q8_rejects():
+    f = lib.spark_kv_append_q8
+    assert f(3, 1, 1, FAKE, FAKE, FAKE, _cache_q8(), None) == 1                  # layer type
+    assert f(0, 1, 0, FAKE, FAKE, FAKE, _cache_q8(), None) == 1                  # n_new
+    assert f(0, 1, 1, FAKE, FAKE, None, _cache_q8(), None) == 1                  # pos
+    assert f(0, 1, 1, FAKE, FAKE, FAKE, _cache_q8(cap=1024), None) == 1          # ring != 512
+    assert f(1, 1, 1, FAKE, FAKE, FAKE, None, None) == 1                         # no cache
+    assert f(1, 1, 1, FAKE, FAKE, FAKE, _cache_q8(ks=None), None) == 1           # no K scales
+    assert f(1, 1, 1, FAKE, FAKE, FAKE, _cache_q8(vs=MISALIGNED), None) == 1     # misaligned
+    assert f(1, 1, 1, FAKE, FAKE, FAKE, _cache_q8(batch=2), None) == 1           # batch
+
+
+def test_decode_q8_rejects():
+    f = lib.spark_attn_decode_q8
+    big = 1 << 30
+    assert f(1, 1, FAKE, FAKE, _cache_q8(cap=64), FAKE, 65, 0, FAKE, big, FAKE, None) == 1  # > capacity
+    assert f(1, 1, FAKE, FAKE, _cache_q8(cap=64), FAKE, 64, -1, FAKE, big, FAKE, None) == 1
+    assert f(1, 1, FAKE, FAKE, _cache_q8(cap=64), FAKE, 64, 2, FAKE, 16, FAKE, None) == 3   # workspace
+    assert f(1, 1, FAKE, FAKE, _cache_q8(cap=64), FAKE, 64, 0, MISALIGNED, big, FAKE, None) == 1
+    assert f(0, 1, FAKE, FAKE, _cache_q8(cap=1024), FAKE, 64, 0, FAKE, big, FAKE, None) == 1
+    assert f(1, 1, FAKE, FAKE, _cache_q8(k=None, cap=64), FAKE, 64, 0, FAKE, big, FAKE, None) == 1
+    assert f(1, 1, FAKE, FAKE, None, FAKE, 64, 0, FAKE, big, FAKE, None) == 1
