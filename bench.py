@@ -132,7 +132,7 @@ def sliding_pairs(S):
 def bench_configs(fga, synth):
     """The other workloads of the hot path's scope table, each timed on its own:
     sliding prefill S=1024; a chunk of 8192 after a cached prefix of 8192 (both layer
-    types); the 36-layer stack at S=32768; batched decode (full, cold
+    types); the 36-layer stack at S=32768; decode over the 8-bit cache; batched decode (full, cold
     caches; sliding ring, warm and cold); long decode at 128K and 1M tokens."""
     import numpy as np
     import torch
@@ -244,6 +244,41 @@ def bench_configs(fga, synth):
         r = decode_case(fga.SLIDING, B, [L] * B, 512, synth.CONFIG_SEED[5] + 10 + B, cold=True)
         out[f"decode_sliding_b{B}_l{L}_cold"] = r
         log(f"config 5 decode sliding B={B} L={L}, cold: {r['us']:.1f} us")
+    # 8-bit (q8_0) cache: 272 bytes per key row and KV head for K and for V, instead of 512.
+    def decode_q8_case(lt, B, lens, cap, seed, cold):
+        lens = np.asarray(lens, dtype=np.int32)
+        gen.manual_seed(seed)
+        qd = dev_normal(gen, (B, 16, 256))
+        gd = dev_normal(gen, (B, 16))
+        codes = lambda: torch.randint(-127, 128, (B, cap, 4, 256), generator=gen, device="cuda", dtype=torch.int8)
+        scales = lambda: (0.005 + 0.025 * torch.rand((B, cap, 4, 8), generator=gen, device="cuda")).half()
+        cache = fga.KVCacheQ8(lt, B, cap, k=codes(), k_scale=scales(), v=codes(), v_scale=scales())
+        sl = torch.as_tensor(lens).cuda()
+        maxlen = int(lens.max())
+        wsd = torch.empty(fga.decode_q8_workspace_bytes(lt, B, maxlen), dtype=torch.uint8, device="cuda")
+        od = torch.empty_like(qd)
+        call = lambda: fga.decode_q8(lt, qd, gd, cache, sl, maxlen, out=od, workspace=wsd)
+        ms = time_each(call, 30, 5, flush if cold else None)
+        vis = np.minimum(lens, 512) if lt == fga.SLIDING else lens
+        nbytes = int(vis.astype(np.int64).sum()) * 4 * 2 * 272 + B * (16 * 256 * 4 + 32)
+        return {"us": ms * 1e3, "gbs": nbytes / (ms * 1e-3) / 1e9,
+                "frac_hbm": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, "bytes": nbytes,
+                "cache": "cold" if cold else "warm", "kv": "q8_0"}
+
+    seed = synth.CONFIG_SEED[3]
+    lens = synth.decode_seq_lens(seed, 64, 1024, 32768)
+    r = decode_q8_case(fga.FULL, 64, lens, 32768, seed + 50, cold=True)
+    out["decode_q8_b64_full_cold"] = r
+    log(f"config 3 decode q8 full, cold: {r['us']:.0f} us  {r['gbs']:.0f} GB/s")
+    torch.cuda.empty_cache()
+    r = decode_q8_case(fga.SLIDING, 64, lens, 512, seed + 51, cold=True)
+    out["decode_q8_b64_sliding_cold"] = r
+    log(f"config 3 decode q8 sliding ring, cold: {r['us']:.1f} us  {r['gbs']:.0f} GB/s")
+    for B, L in ((4, 131072), (1, 1 << 20)):
+        r = decode_q8_case(fga.FULL, B, [L] * B, L, synth.CONFIG_SEED[5] + 60 + B, cold=True)
+        out[f"decode_q8_full_b{B}_l{L}_cold"] = r
+        log(f"config 5 decode q8 full B={B} L={L}, cold: {r['us']:.0f} us  {r['gbs']:.0f} GB/s")
+        torch.cuda.empty_cache()
     del flush_a
     torch.cuda.empty_cache()
     return out

@@ -65,6 +65,8 @@ def _load():
     q8_p = ctypes.POINTER(KvCacheQ8Desc)
     lib.spark_kv_append_q8.argtypes = [i32, i32, i32, vp, vp, vp, q8_p, vp]
     lib.spark_kv_append_q8.restype = i32
+    lib.spark_attn_decode_q8_workspace_bytes.argtypes = [i32, i32, i32, i32]
+    lib.spark_attn_decode_q8_workspace_bytes.restype = sz
     lib.spark_attn_decode_q8.argtypes = [i32, i32, vp, vp, q8_p, vp, i32, i32, vp, sz, vp, vp]
     lib.spark_attn_decode_q8.restype = i32
     lib.spark_status_string.argtypes = [i32]
@@ -78,7 +80,7 @@ _lib = _load()
 
 LIBRARY_PATH = _LIB_PATH
 EXPORTED = ("spark_attn_prefill_workspace_bytes", "spark_attn_prefill", "spark_kv_append", "spark_attn_decode_workspace_bytes",
-            "spark_attn_decode", "spark_kv_append_q8", "spark_attn_decode_q8", "spark_status_string",
+            "spark_attn_decode", "spark_kv_append_q8", "spark_attn_decode_q8_workspace_bytes", "spark_attn_decode_q8", "spark_status_string",
             "spark_abi_version")
 
 
@@ -274,6 +276,11 @@ def kv_append_q8(layer_type: int, k, v, pos, cache: KVCacheQ8, stream=None):
         raise SparkError(st, "spark_kv_append_q8")
 
 
+def decode_q8_workspace_bytes(layer_type: int, batch: int, max_seq_len: int, num_parts: int = 0) -> int:
+    return int(_lib.spark_attn_decode_q8_workspace_bytes(int(layer_type), int(batch), int(max_seq_len),
+                                                         int(num_parts)))
+
+
 def decode_q8(layer_type: int, q, gate, cache: KVCacheQ8, seq_lens, max_seq_len: int, out=None,
               workspace=None, num_parts: int = 0, stream=None):
     """spark_attn_decode_q8: decode against an 8-bit cache; arguments as for decode."""
@@ -284,7 +291,7 @@ def decode_q8(layer_type: int, q, gate, cache: KVCacheQ8, seq_lens, max_seq_len:
     _check(seq_lens, "seq_lens", (B,), torch.int32)
     if cache.layer_type != layer_type:
         raise ValueError("cache layer type differs from the call's")
-    need = decode_workspace_bytes(layer_type, B, max_seq_len, num_parts)
+    need = decode_q8_workspace_bytes(layer_type, B, max_seq_len, num_parts)
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
     _check(workspace, "workspace", None, torch.uint8)

@@ -208,6 +208,14 @@ spark_status spark_kv_append_q8(int32_t layer_type, int32_t batch, int32_t n_new
   return from_hip(spark::launch_append_q8(layer_type, a, static_cast<hipStream_t>(stream)));
 }
 
+size_t spark_attn_decode_q8_workspace_bytes(int32_t layer_type, int32_t batch, int32_t max_seq_len,
+                                            int32_t num_parts) {
+  if (!valid_type(layer_type) || batch < 1 || batch > kMaxBatch || max_seq_len < 1 ||
+      max_seq_len > kMaxSeq || num_parts < 0 || num_parts > kMaxParts)
+    return 0;
+  return spark::plan_decode(layer_type, batch, max_seq_len, num_parts, true).total_bytes;
+}
+
 spark_status spark_attn_decode_q8(int32_t layer_type, int32_t batch, const void* q,
                                   const void* gate_logits, const spark_kv_cache_q8* cache,
                                   const int32_t* seq_lens, int32_t max_seq_len,
@@ -219,7 +227,7 @@ spark_status spark_attn_decode_q8(int32_t layer_type, int32_t batch, const void*
   st = check_cache_q8(layer_type, cache, batch);
   if (st != SPARK_OK) return st;
   if (layer_type == SPARK_LAYER_FULL && max_seq_len > cache->capacity) return SPARK_ERR_INVALID_ARG;
-  const spark::DecodePlan plan = spark::plan_decode(layer_type, batch, max_seq_len, num_parts);
+  const spark::DecodePlan plan = spark::plan_decode(layer_type, batch, max_seq_len, num_parts, true);
   if (workspace_bytes < plan.total_bytes) return SPARK_ERR_WORKSPACE;
   spark::DecodeArgs a = decode_args(plan, batch, cache->capacity, q, gate_logits, seq_lens, workspace, out);
   a.k_codes = static_cast<const int8_t*>(cache->k);

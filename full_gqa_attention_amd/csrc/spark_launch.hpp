@@ -86,6 +86,6 @@ struct DecodePlan {
   size_t ml_offset;
   size_t total_bytes;
 };
-DecodePlan plan_decode(int layer_type, int batch, int max_seq_len, int nparts);
+DecodePlan plan_decode(int layer_type, int batch, int max_seq_len, int nparts, bool q8 = false);
 
 }  // namespace spark

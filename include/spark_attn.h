@@ -198,10 +198,18 @@ spark_status spark_kv_append_q8(int32_t layer_type, int32_t batch, int32_t n_new
                                 const spark_kv_cache_q8* cache, void* stream);
 
 /*
+ * Bytes of device workspace spark_attn_decode_q8 needs; as
+ * spark_attn_decode_workspace_bytes, except that num_parts = 0 plans two partitions per
+ * CU (one for the bf16 cache).
+ */
+size_t spark_attn_decode_q8_workspace_bytes(int32_t layer_type, int32_t batch,
+                                            int32_t max_seq_len, int32_t num_parts);
+
+/*
  * spark_attn_decode against an 8-bit cache: keys and values read back as code * scale.
- * Same arguments, limits, workspace (size from spark_attn_decode_workspace_bytes) and
- * errors as spark_attn_decode; the two launches stream 272 + 272 bytes per key and KV
- * head instead of 512 + 512.
+ * Same arguments, limits and errors as spark_attn_decode, with the workspace of
+ * spark_attn_decode_q8_workspace_bytes; the two launches stream 272 + 272 bytes per key
+ * and KV head instead of 512 + 512.
  */
 spark_status spark_attn_decode_q8(int32_t layer_type, int32_t batch, const void* q,
                                   const void* gate_logits, const spark_kv_cache_q8* cache,

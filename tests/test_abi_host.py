@@ -141,3 +141,11 @@ def test_decode_q8_rejects():
     assert f(0, 1, FAKE, FAKE, _cache_q8(cap=1024), FAKE, 64, 0, FAKE, big, FAKE, None) == 1
     assert f(1, 1, FAKE, FAKE, _cache_q8(k=None, cap=64), FAKE, 64, 0, FAKE, big, FAKE, None) == 1
     assert f(1, 1, FAKE, FAKE, None, FAKE, 64, 0, FAKE, big, FAKE, None) == 1
+
+
+def test_workspace_planning_q8():
+    ws = fga.decode_q8_workspace_bytes
+    assert ws(1, 1, 64, 2) == _layout_bytes(1, 2)
+    assert ws(1, 64, 32768) == _layout_bytes(64, 512)     # two partitions per CU (256 on the host)
+    assert ws(0, 1, 100000) == _layout_bytes(1, 16)       # never more than the chunks
+    assert ws(2, 1, 64) == 0 and ws(1, 1, 64, -1) == 0
