@@ -38,6 +38,7 @@ from .attention import (  # noqa: F401
     layer_types,
     prefill,
     prefill_chunk,
+    prefill_varlen,
     rope,
     rope_inv_freq,
     round_to_bf16_bits,

@@ -251,6 +251,27 @@ def prefill_chunk(q, k, v, gate, cache_k, cache_v, start_pos: int, layer_type, r
     return out
 
 
+def prefill_varlen(q, k, v, gate, cu_seqlens, layer_type, rows=None) -> np.ndarray:
+    """Prefill of sequences packed back to back: sequence b owns token rows
+    cu_seqlens[b] .. cu_seqlens[b+1]-1, its token t sits at position t, and it attends
+    only to itself -- each sequence is the one-sequence ``prefill`` of its own rows.
+    q [T,16,256], k/v [T,4,256], gate [T,16]; ``rows`` are packed row indices (default
+    all).  Returns float64 [len(rows), 16, 256].
+    """
+    cu = [int(x) for x in cu_seqlens]
+    T = np.asarray(q).shape[0]
+    rows = np.arange(T) if rows is None else np.asarray(rows, dtype=np.int64)
+    out = np.zeros((len(rows),) + np.asarray(q).shape[1:], dtype=np.float64)
+    for b in range(len(cu) - 1):
+        lo, hi = cu[b], cu[b + 1]
+        sel = np.nonzero((rows >= lo) & (rows < hi))[0]
+        if hi <= lo or len(sel) == 0:
+            continue
+        one = lambda x: np.asarray(x)[lo:hi][None]
+        out[sel] = prefill(one(q), one(k), one(v), one(gate), layer_type, rows=rows[sel] - lo)[0]
+    return out
+
+
 def cache_slot(position: int, layer_type: int, window: int = WINDOW) -> int:
     """Cache slot of a position: itself on full layers, position mod 512 on sliding layers.
 

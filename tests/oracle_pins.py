@@ -455,6 +455,47 @@ def pin_chunked_matches_one_shot(att):
         assert np.max(np.abs(got - want)) < 2e-2, f"chunked vs one-shot lt={lt}: max abs"
 
 
+def pin_varlen_equal_lengths_is_batched(att):
+    """Sequences of equal length packed back to back give the batched prefill's rows."""
+    rng = np.random.default_rng(61)
+    B, S = 3, 40
+    x = {n: att.round_to_bf16_bits(rng.standard_normal(sh)) for n, sh in
+         (("q", (B, S, 16, 256)), ("k", (B, S, 4, 256)), ("v", (B, S, 4, 256)), ("gate", (B, S, 16)))}
+    for lt in (att.SLIDING, att.FULL):
+        want = att.prefill(x["q"], x["k"], x["v"], x["gate"], lt).reshape(B * S, 16, 256)
+        packed = {n: a.reshape((B * S,) + a.shape[2:]) for n, a in x.items()}
+        got = att.prefill_varlen(packed["q"], packed["k"], packed["v"], packed["gate"], [0, S, 2 * S, 3 * S], lt)
+        _close(got, want, 0.0, f"varlen equal lengths lt={lt}")
+
+
+def pin_varlen_isolation(att):
+    """A sequence's rows depend on its own tokens only: changing every other sequence (and
+    inserting empty ones) leaves them unchanged, and its rows start again at position 0."""
+    rng = np.random.default_rng(62)
+    lens = [5, 0, 37, 1, 20]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    T = int(cu[-1])
+    x = {n: att.round_to_bf16_bits(rng.standard_normal(sh)) for n, sh in
+         (("q", (T, 16, 256)), ("k", (T, 4, 256)), ("v", (T, 4, 256)), ("gate", (T, 16)))}
+    for lt in (att.SLIDING, att.FULL):
+        base = att.prefill_varlen(x["q"], x["k"], x["v"], x["gate"], cu, lt)
+        y = {n: a.copy() for n, a in x.items()}
+        mine = slice(int(cu[2]), int(cu[3]))
+        for n in y:
+            other = np.ones(T, bool)
+            other[mine] = False
+            y[n][other] = att.round_to_bf16_bits(rng.standard_normal(y[n][other].shape))
+        got = att.prefill_varlen(y["q"], y["k"], y["v"], y["gate"], cu, lt)
+        _close(got[mine], base[mine], 0.0, f"isolation lt={lt}")
+        alone = att.prefill(x["q"][mine][None], x["k"][mine][None], x["v"][mine][None], x["gate"][mine][None], lt)[0]
+        _close(base[mine], alone, 0.0, f"positions restart lt={lt}")
+        # row 0 of a sequence is sigma(g) v0 of that sequence
+        g0 = att.bf16_to_f64(x["gate"][cu[2]])
+        v0 = att.bf16_to_f64(x["v"][cu[2]])
+        want0 = (1 / (1 + np.exp(-g0)))[:, None] * np.repeat(v0, 4, axis=0)
+        _close(base[cu[2]], want0, 1e-12, f"first row lt={lt}")
+
+
 # --------------------------------------------------------------------------- footprint
 
 
@@ -612,5 +653,5 @@ ALL_PINS = [
     pin_rope_properties, pin_rope_frequencies, pin_layer_schedule, pin_bf16_rounding,
     pin_kv_append, pin_decode_brute, pin_decode_matches_prefill_row,
     pin_chunk_start_zero_is_prefill, pin_chunk_brute_force, pin_chunk_ignores_out_of_reach_slots,
-    pin_chunked_matches_one_shot,
+    pin_chunked_matches_one_shot, pin_varlen_equal_lengths_is_batched, pin_varlen_isolation,
 ]

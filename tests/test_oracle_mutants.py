@@ -34,6 +34,9 @@ MUTANTS = {
     "chunk_key_positions": ("new_pos = P + np.arange(n)", "new_pos = np.arange(n) + 1"),
     "chunk_history_from_keys": ("bf16_to_f64(np.asarray(cache_v)[b, h_slot])", "bf16_to_f64(np.asarray(cache_k)[b, h_slot])"),
     "chunk_history_one_short": ("h_pos = np.arange(h_lo, P)", "h_pos = np.arange(h_lo + 1, P)"),
+    "varlen_sequence_starts_early": ("one = lambda x: np.asarray(x)[lo:hi][None]",
+                                     "one = lambda x: np.asarray(x)[max(lo - 1, 0):hi - 1 if lo > 0 else hi][None]"),
+    "varlen_skips_single_token": ("if hi <= lo or len(sel) == 0:", "if hi <= lo + 1 or len(sel) == 0:"),
 }
 
 
