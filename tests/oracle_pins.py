@@ -489,11 +489,14 @@ def pin_varlen_isolation(att):
         _close(got[mine], base[mine], 0.0, f"isolation lt={lt}")
         alone = att.prefill(x["q"][mine][None], x["k"][mine][None], x["v"][mine][None], x["gate"][mine][None], lt)[0]
         _close(base[mine], alone, 0.0, f"positions restart lt={lt}")
-        # row 0 of a sequence is sigma(g) v0 of that sequence
-        g0 = att.bf16_to_f64(x["gate"][cu[2]])
-        v0 = att.bf16_to_f64(x["v"][cu[2]])
-        want0 = (1 / (1 + np.exp(-g0)))[:, None] * np.repeat(v0, 4, axis=0)
-        _close(base[cu[2]], want0, 1e-12, f"first row lt={lt}")
+        # row 0 of every non-empty sequence is sigma(g) v0 of that sequence
+        for b in range(len(lens)):
+            if lens[b] == 0:
+                continue
+            g0 = att.bf16_to_f64(x["gate"][cu[b]])
+            v0 = att.bf16_to_f64(x["v"][cu[b]])
+            want0 = (1 / (1 + np.exp(-g0)))[:, None] * np.repeat(v0, 4, axis=0)
+            _close(base[cu[b]], want0, 1e-12, f"first row of sequence {b} lt={lt}")
 
 
 # --------------------------------------------------------------------------- footprint
