@@ -56,6 +56,10 @@ def _load():
     lib.spark_attn_prefill_workspace_bytes.restype = sz
     lib.spark_attn_prefill.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp, cache_p, vp, sz, vp, vp]
     lib.spark_attn_prefill.restype = i32
+    lib.spark_attn_prefill_varlen_workspace_bytes.argtypes = [i32, i32]
+    lib.spark_attn_prefill_varlen_workspace_bytes.restype = sz
+    lib.spark_attn_prefill_varlen.argtypes = [i32, i32, vp, i32, i32, vp, vp, vp, vp, cache_p, vp, sz, vp, vp]
+    lib.spark_attn_prefill_varlen.restype = i32
     lib.spark_kv_append.argtypes = [i32, i32, i32, vp, vp, vp, cache_p, vp]
     lib.spark_kv_append.restype = i32
     lib.spark_attn_decode_workspace_bytes.argtypes = [i32, i32, i32, i32]
@@ -79,7 +83,8 @@ def _load():
 _lib = _load()
 
 LIBRARY_PATH = _LIB_PATH
-EXPORTED = ("spark_attn_prefill_workspace_bytes", "spark_attn_prefill", "spark_kv_append", "spark_attn_decode_workspace_bytes",
+EXPORTED = ("spark_attn_prefill_workspace_bytes", "spark_attn_prefill", "spark_attn_prefill_varlen_workspace_bytes",
+            "spark_attn_prefill_varlen", "spark_kv_append", "spark_attn_decode_workspace_bytes",
             "spark_attn_decode", "spark_kv_append_q8", "spark_attn_decode_q8_workspace_bytes", "spark_attn_decode_q8", "spark_status_string",
             "spark_abi_version")
 
@@ -212,6 +217,42 @@ def prefill(layer_type: int, q, k, v, gate, out=None, cache: KVCache | None = No
                                  _ptr(out), _stream(stream))
     if st:
         raise SparkError(st, "spark_attn_prefill")
+    return out
+
+
+def prefill_varlen_workspace_bytes(layer_type: int, total_tokens: int) -> int:
+    return int(_lib.spark_attn_prefill_varlen_workspace_bytes(int(layer_type), int(total_tokens)))
+
+
+def prefill_varlen(layer_type: int, q, k, v, gate, cu_seqlens, max_seqlen: int, out=None,
+                   cache: KVCache | None = None, workspace=None, stream=None):
+    """spark_attn_prefill_varlen: sequences packed back to back, q [T,16,256], k/v [T,4,256],
+    gate [T,16] (bf16, pre-RoPE); cu_seqlens device int32 [B+1] of token offsets."""
+    torch = _torch()
+    T = int(q.shape[0])
+    _check(q, "q", (T, N_Q_HEADS, HEAD_DIM), torch.bfloat16)
+    _check(k, "k", (T, N_KV_HEADS, HEAD_DIM), torch.bfloat16)
+    _check(v, "v", (T, N_KV_HEADS, HEAD_DIM), torch.bfloat16)
+    _check(gate, "gate", (T, N_Q_HEADS), torch.bfloat16)
+    _check(cu_seqlens, "cu_seqlens", None, torch.int32)
+    B = int(cu_seqlens.shape[0]) - 1
+    if out is None:
+        out = torch.empty_like(q)
+    _check(out, "out", tuple(q.shape), torch.bfloat16)
+    desc = None
+    if cache is not None:
+        if cache.layer_type != layer_type:
+            raise ValueError("cache layer type differs from the call's")
+        desc = ctypes.pointer(cache.desc())
+    if workspace is None:
+        workspace = torch.empty(max(prefill_varlen_workspace_bytes(layer_type, T), 256), dtype=torch.uint8,
+                                device=q.device)
+    _check(workspace, "workspace", None, torch.uint8)
+    st = _lib.spark_attn_prefill_varlen(int(layer_type), B, _ptr(cu_seqlens), T, int(max_seqlen), _ptr(q),
+                                        _ptr(k), _ptr(v), _ptr(gate), desc, _ptr(workspace),
+                                        int(workspace.numel()), _ptr(out), _stream(stream))
+    if st:
+        raise SparkError(st, "spark_attn_prefill_varlen")
     return out
 
 

@@ -126,11 +126,60 @@ spark_status spark_attn_prefill(int32_t layer_type, int32_t batch, int32_t seq_l
   a.out = static_cast<uint16_t*>(out);
   a.cache_k = cache ? static_cast<uint16_t*>(cache->k) : nullptr;
   a.cache_v = cache ? static_cast<uint16_t*>(cache->v) : nullptr;
+  a.cu_seqlens = nullptr;
+  a.total_tokens = batch * seq_len;
   a.batch = batch;
   a.seq_len = seq_len;
   a.cache_cap = cache ? cache->capacity : 0;
   a.nqb = (int)nqb;
   a.start_pos = start_pos;
+  return from_hip(spark::launch_prefill(layer_type, a, static_cast<hipStream_t>(stream)));
+}
+
+size_t spark_attn_prefill_varlen_workspace_bytes(int32_t layer_type, int32_t total_tokens) {
+  if (!valid_type(layer_type) || total_tokens < 1) return 0;
+  return spark::prefill_workspace_bytes(1, total_tokens);
+}
+
+spark_status spark_attn_prefill_varlen(int32_t layer_type, int32_t batch, const int32_t* cu_seqlens,
+                                       int32_t total_tokens, int32_t max_seqlen, const void* q,
+                                       const void* k, const void* v, const void* gate_logits,
+                                       const spark_kv_cache* cache, void* workspace,
+                                       size_t workspace_bytes, void* out, void* stream) {
+  if (!valid_type(layer_type)) return SPARK_ERR_INVALID_ARG;
+  if (batch < 1 || batch > kMaxBatch || max_seqlen < 1 || max_seqlen > kMaxSeq || total_tokens < 1)
+    return SPARK_ERR_INVALID_ARG;
+  // Grid as for a uniform batch of max_seqlen: ceil(max_seqlen / 64) * batch * 4 workgroups.
+  if ((long long)batch * max_seqlen > 0xfffffffeLL) return SPARK_ERR_INVALID_ARG;
+  if (!cu_seqlens || (reinterpret_cast<uintptr_t>(cu_seqlens) & 3u)) return SPARK_ERR_INVALID_ARG;
+  if (!q || !k || !v || !gate_logits || !out) return SPARK_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned2(gate_logits))
+    return SPARK_ERR_INVALID_ARG;
+  if (cache) {
+    const spark_status cs = check_cache(layer_type, cache, batch);
+    if (cs != SPARK_OK) return cs;
+    if (layer_type == SPARK_LAYER_FULL && cache->capacity < max_seqlen) return SPARK_ERR_INVALID_ARG;
+  }
+  if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u)) return SPARK_ERR_INVALID_ARG;
+  if (workspace_bytes < spark::prefill_workspace_bytes(1, total_tokens)) return SPARK_ERR_WORKSPACE;
+  const int rows = spark::prefill_block_rows();
+
+  spark::PrefillArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.k_rot = static_cast<uint16_t*>(workspace);
+  a.gate = static_cast<const uint16_t*>(gate_logits);
+  a.out = static_cast<uint16_t*>(out);
+  a.cache_k = cache ? static_cast<uint16_t*>(cache->k) : nullptr;
+  a.cache_v = cache ? static_cast<uint16_t*>(cache->v) : nullptr;
+  a.cu_seqlens = cu_seqlens;
+  a.total_tokens = total_tokens;
+  a.batch = batch;
+  a.seq_len = max_seqlen;
+  a.cache_cap = cache ? cache->capacity : 0;
+  a.nqb = (max_seqlen + rows - 1) / rows;
+  a.start_pos = 0;
   return from_hip(spark::launch_prefill(layer_type, a, static_cast<hipStream_t>(stream)));
 }
 

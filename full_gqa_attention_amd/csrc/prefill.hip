@@ -116,8 +116,23 @@ __device__ __forceinline__ size_t prefix_row(const PrefillArgs& a, int b, int g,
   const int slot = LT == kFull ? p : (p & (kWindow - 1));
   return (((size_t)b * a.cache_cap + slot) * kKvHeads + g) * kHeadDim;
 }
-__device__ __forceinline__ size_t chunk_row(const PrefillArgs& a, int b, int g, int p, int P) {
-  return (((size_t)b * a.seq_len + (p - P)) * kKvHeads + g) * kHeadDim;
+// Token rows of sequence b: first row and length.  Uniform batches are b * S and S;
+// varlen batches read cu_seqlens, clamped so that a malformed table can only shorten a
+// sequence, never move an access outside the T rows or beyond the largest length.
+struct SeqSpan {
+  size_t row0;
+  int len;
+};
+__device__ __forceinline__ SeqSpan seq_span(const PrefillArgs& a, int b) {
+  if (a.cu_seqlens == nullptr) return {(size_t)b * a.seq_len, a.seq_len};
+  const int T = a.total_tokens;
+  const int lo = min(max(a.cu_seqlens[b], 0), T);
+  const int hi = min(max(a.cu_seqlens[b + 1], lo), min(T, lo + a.seq_len));
+  return {(size_t)lo, hi - lo};
+}
+
+__device__ __forceinline__ size_t chunk_row(const SeqSpan& sp, int g, int p, int P) {
+  return ((sp.row0 + (p - P)) * kKvHeads + g) * kHeadDim;
 }
 
 // Load instruction i of tile (keys k0 .. k0+31, absolute positions) of (sequence b, KV
@@ -133,16 +148,16 @@ __device__ __forceinline__ size_t chunk_row(const PrefillArgs& a, int b, int g, 
 // wholly inside the chunk picks its source once and only a tile across start_pos selects
 // per lane; there the scalar-base form was 2-5% slower (both forms in one kernel).
 template <int LT, bool PFX>
-__device__ __forceinline__ void issue_one(const PrefillArgs& a, int b, int g, int k0, int wave,
-                                          int lane, uint8_t* ks, uint8_t* vs, int i) {
+__device__ __forceinline__ void issue_one(const PrefillArgs& a, int b, const SeqSpan& sp, int g, int k0,
+                                          int wave, int lane, uint8_t* ks, uint8_t* vs, int i) {
   const int P = PFX ? a.start_pos : 0;
-  const int kend = P + a.seq_len;
+  const int kend = P + sp.len;
   const bool in_chunk = !PFX || k0 >= P, in_prefix = k0 + kBN <= P;   // wave-uniform
   if (!PFX) {
     static_assert(kKLoads == 2 && kVLoads == 2, "offsets below assume 8 waves");
     const int h = lane >> 5, l31 = lane & 31;
     const int lim = kend - 1 - k0;                  // last readable row of the tile
-    const size_t base = ((((size_t)b * a.seq_len + k0) * kKvHeads + g) * kHeadDim) * 2;   // bytes
+    const size_t base = (((sp.row0 + k0) * kKvHeads + g) * kHeadDim) * 2;   // bytes
     if (i < kKLoads) {
       const uint8_t* src = (const uint8_t*)a.k_rot + base + 64 * wave;
       dma16_s(src, (uint32_t)(min(l31, lim) * 2048 + 16 * h + 32 * i), ks + (kKLoads * wave + i) * 1024);
@@ -160,7 +175,7 @@ __device__ __forceinline__ void issue_one(const PrefillArgs& a, int b, int g, in
     const int off = 8 * (2 * n + (lane >> 5));
     const bool from_cache = !in_chunk && (in_prefix || pk < P);
     const uint16_t* base = from_cache ? a.cache_k : a.k_rot;
-    const size_t row = from_cache ? prefix_row<LT>(a, b, g, pk) : chunk_row(a, b, g, pk, P);
+    const size_t row = from_cache ? prefix_row<LT>(a, b, g, pk) : chunk_row(sp, g, pk, P);
     dma16(base + (row + off), ks + n * 1024);
   } else {
     const int n = kVLoads * wave + (i - kKLoads);
@@ -169,15 +184,15 @@ __device__ __forceinline__ void issue_one(const PrefillArgs& a, int b, int g, in
     const int p = min(k0 + r, kend - 1);
     const bool from_cache = !in_chunk && (in_prefix || p < P);
     const uint16_t* base = from_cache ? a.cache_v : a.v;
-    const size_t row = from_cache ? prefix_row<LT>(a, b, g, p) : chunk_row(a, b, g, p, P);
+    const size_t row = from_cache ? prefix_row<LT>(a, b, g, p) : chunk_row(sp, g, p, P);
     dma16(base + (row + off), vs + n * 1024);
   }
 }
 template <int LT, bool PFX>
-__device__ __forceinline__ void issue_tile(const PrefillArgs& a, int b, int g, int k0, int wave,
-                                           int lane, uint8_t* ks, uint8_t* vs) {
+__device__ __forceinline__ void issue_tile(const PrefillArgs& a, int b, const SeqSpan& sp, int g, int k0,
+                                           int wave, int lane, uint8_t* ks, uint8_t* vs) {
 #pragma unroll
-  for (int i = 0; i < kKLoads + kVLoads; ++i) issue_one<LT, PFX>(a, b, g, k0, wave, lane, ks, vs, i);
+  for (int i = 0; i < kKLoads + kVLoads; ++i) issue_one<LT, PFX>(a, b, sp, g, k0, wave, lane, ks, vs, i);
 }
 
 // RoPE of the chunk's K, once per position p = P + t: k_rot = R_p(k) (rotate-half form:
@@ -197,12 +212,15 @@ __global__ __launch_bounds__(256) void prefill_rope_kernel(PrefillArgs a) {
   __shared__ double s_inv[T::kRot / 2];
   if (threadIdx.x < T::kRot / 2) s_inv[threadIdx.x] = rope_inv_rev(threadIdx.x, T::kRot, log2(T::kTheta));
   __syncthreads();
-  const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const size_t nrows = (size_t)a.batch * a.seq_len * kKvHeads;
-  const size_t row = idx >> 5;                       // (b * S + p) * 4 + g
-  const int c = (int)(idx & 31);
-  if (row >= nrows) return;
-  const int p = a.start_pos + (int)((row / kKvHeads) % a.seq_len);
+  // Grid: x = tokens of a sequence (two per workgroup), y = sequence.
+  const int b = blockIdx.y;
+  const SeqSpan sp = seq_span(a, b);
+  const int t = (int)((blockIdx.x * blockDim.x + threadIdx.x) >> 7);   // token within the sequence
+  const int g = (threadIdx.x >> 5) & 3;
+  const int c = threadIdx.x & 31;
+  if (t >= sp.len) return;
+  const size_t row = (sp.row0 + t) * kKvHeads + g;
+  const int p = a.start_pos + t;
   const uint16_t* krow = a.k + row * kHeadDim;
   const u32x4 x = ld_global16(krow + 8 * c);
   u32x4 y = x;
@@ -222,10 +240,8 @@ __global__ __launch_bounds__(256) void prefill_rope_kernel(PrefillArgs a) {
     }
   }
   st_global16(a.k_rot + row * kHeadDim + 8 * c, y);
-  if (a.cache_k != nullptr && (LT == kFull || (a.start_pos == 0 && p >= a.seq_len - kWindow))) {
+  if (a.cache_k != nullptr && (LT == kFull || (a.start_pos == 0 && t >= sp.len - kWindow))) {
     const int slot = LT == kFull ? p : (p & (kWindow - 1));
-    const size_t b = row / ((size_t)kKvHeads * a.seq_len);
-    const int g = (int)(row % kKvHeads);
     const size_t dst = (((size_t)b * a.cache_cap + slot) * kKvHeads + g) * kHeadDim + 8 * c;
     st_global16(a.cache_k + dst, y);
     st_global16(a.cache_v + dst, ld_global16(a.v + row * kHeadDim + 8 * c));
@@ -278,13 +294,12 @@ __device__ __forceinline__ void block_coords(int id, int batch, int nqb, int& b,
 // Rotate (RoPE at position p) and scale the Q row slice this lane holds, into MFMA
 // B-operand fragments: fragment s holds dims 16s + 8*half + j.
 template <int LT>
-__device__ __forceinline__ void load_q(const PrefillArgs& a, int b, int hq, int row, int pos0,
+__device__ __forceinline__ void load_q(const PrefillArgs& a, const SeqSpan& sp, int hq, int row, int pos0,
                                        int half, const double* inv, bf16x8* qf) {
   using T = LayerTraits<LT>;
-  const int S = a.seq_len;
   u32x4 raw[16];
-  if (row < S) {
-    const uint16_t* qrow = a.q + (((size_t)b * S + row) * kQHeads + hq) * kHeadDim;
+  if (row < sp.len) {
+    const uint16_t* qrow = a.q + ((sp.row0 + row) * kQHeads + hq) * kHeadDim;
 #pragma unroll
     for (int s = 0; s < 16; ++s) raw[s] = ld_global16(qrow + 16 * s + 8 * half);
   } else {
@@ -339,12 +354,14 @@ void prefill_kernel(PrefillArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // scalar: wave-uniform branches
   const int half = lane >> 5;
   const int r32 = lane & 31;
-  const int S = a.seq_len;                  // chunk rows
   const int P = PFX ? a.start_pos : 0;      // position of chunk row 0
 
   int b, g, qb;
   block_coords<LT>(blockIdx.x, a.batch, a.nqb, b, g, qb);
   const int q0 = qb * kBM;
+  const SeqSpan sp = seq_span(a, b);
+  const int S = sp.len;                     // chunk rows of this sequence
+  if (q0 >= S) return;                      // varlen: a shorter sequence (whole workgroup)
   const int hq = g * kGroup + (kRowBlocks == 2 ? wave : wave >> 1);
   const int rb0 = kRowBlocks == 2 ? 0 : (wave & 1);      // first 32-row block of this wave
 
@@ -354,8 +371,8 @@ void prefill_kernel(PrefillArgs a) {
   const int kt_hi = hi_key / kBN;
 
   // Start streaming the first two tiles before anything else.
-  issue_tile<LT, PFX>(a, b, g, kt_lo * kBN, wave, lane, s_k0, s_v0);
-  if (kt_lo + 1 <= kt_hi) issue_tile<LT, PFX>(a, b, g, (kt_lo + 1) * kBN, wave, lane, s_k1, s_v1);
+  issue_tile<LT, PFX>(a, b, sp, g, kt_lo * kBN, wave, lane, s_k0, s_v0);
+  if (kt_lo + 1 <= kt_hi) issue_tile<LT, PFX>(a, b, sp, g, (kt_lo + 1) * kBN, wave, lane, s_k1, s_v1);
 
   if (tid < T::kRot / 2) s_inv[tid] = rope_inv_rev(tid, T::kRot, log2(T::kTheta));
   barrier_lds();
@@ -363,7 +380,7 @@ void prefill_kernel(PrefillArgs a) {
   // Q fragments of both 32-row blocks: lane holds row r32 of each.
   bf16x8 qf[kRowBlocks][16];
 #pragma unroll
-  for (int rb = 0; rb < kRowBlocks; ++rb) load_q<LT>(a, b, hq, q0 + 32 * (rb0 + rb) + r32, P, half, s_inv, qf[rb]);
+  for (int rb = 0; rb < kRowBlocks; ++rb) load_q<LT>(a, sp, hq, q0 + 32 * (rb0 + rb) + r32, P, half, s_inv, qf[rb]);
 
   // First tiles: wait for this lane's loads (of both), publish.
   wait_vmcnt<0>();
@@ -420,7 +437,7 @@ void prefill_kernel(PrefillArgs a) {
         const bf16x8 ka = as_bf16x8(*reinterpret_cast<const u32x4*>(ks + (32 * (2 * s + half) + r32) * 16));
 #pragma unroll
         for (int rb = 0; rb < kRowBlocks; ++rb) sacc[rb] = mfma_32x32x16(ka, qf[rb][s], sacc[rb]);
-        if (ST != 0 && two_ahead && (s & 3) == 1) issue_one<LT, PFX>(a, b, g, k0 + 2 * kBN, wave, lane, ks2, vs2, s >> 2);
+        if (ST != 0 && two_ahead && (s & 3) == 1) issue_one<LT, PFX>(a, b, sp, g, k0 + 2 * kBN, wave, lane, ks2, vs2, s >> 2);
       }
       bf16x8 pf[kRowBlocks][2];
 #pragma unroll
@@ -476,7 +493,7 @@ void prefill_kernel(PrefillArgs a) {
     }
     // Step 0 issues its prefetch after the MFMAs; the others issue it one instruction every
     // four QK MFMAs, or here when this wave's rows see no key of the tile.
-    if (two_ahead && (ST == 0 || !any_rb)) issue_tile<LT, PFX>(a, b, g, k0 + 2 * kBN, wave, lane, ks2, vs2);
+    if (two_ahead && (ST == 0 || !any_rb)) issue_tile<LT, PFX>(a, b, sp, g, k0 + 2 * kBN, wave, lane, ks2, vs2);
     if (kt + 1 <= kt_hi) {
       // This lane's loads of tile kt+1 were issued one step ago; tile kt+2's may still be
       // in flight.  Every lane waits for its own loads before the barrier: other waves
@@ -506,7 +523,7 @@ void prefill_kernel(PrefillArgs a) {
     // Row pitch 264 bytes keeps the 8-byte writes of the 32 rows on distinct banks.
     const int row = q0 + 32 * rb0 + r32;
     const float l_tot = l_part[0] + __shfl_xor(l_part[0], 32);
-    const float gl = row < S ? bf16_to_f32(a.gate[((size_t)b * S + row) * kQHeads + hq]) : 0.0f;
+    const float gl = row < S ? bf16_to_f32(a.gate[(sp.row0 + row) * kQHeads + hq]) : 0.0f;
     const float scale = sigmoidf_fast(gl) / l_tot;
     constexpr int kPitch = 264;
     uint8_t* const stage = &s_ring[0][0][0] + wave * (32 * kPitch);   // 8 x 8448 B of 96 KB
@@ -531,7 +548,7 @@ void prefill_kernel(PrefillArgs a) {
         const u32x4 x = *reinterpret_cast<const u32x4*>(stage + rr * kPitch + c * 16);
         const int grow = q0 + 32 * rb0 + rr;
         if (grow < S)
-          *reinterpret_cast<u32x4*>(a.out + (((size_t)b * S + grow) * kQHeads + hq) * kHeadDim + 128 * r + 8 * c) = x;
+          *reinterpret_cast<u32x4*>(a.out + ((sp.row0 + grow) * kQHeads + hq) * kHeadDim + 128 * r + 8 * c) = x;
       }
       __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4));   // reads done before reuse
       __builtin_amdgcn_wave_barrier();
@@ -542,9 +559,9 @@ void prefill_kernel(PrefillArgs a) {
       const int row = q0 + 32 * (rb0 + rb) + r32;
       const float l_tot = l_part[rb] + __shfl_xor(l_part[rb], 32);
       if (row < S) {
-        const float gl = bf16_to_f32(a.gate[((size_t)b * S + row) * kQHeads + hq]);
+        const float gl = bf16_to_f32(a.gate[(sp.row0 + row) * kQHeads + hq]);
         const float scale = sigmoidf_fast(gl) / l_tot;
-        uint16_t* orow = a.out + (((size_t)b * S + row) * kQHeads + hq) * kHeadDim;
+        uint16_t* orow = a.out + ((sp.row0 + row) * kQHeads + hq) * kHeadDim;
 #pragma unroll
         for (int db = 0; db < 8; ++db) {
 #pragma unroll
@@ -564,8 +581,7 @@ void prefill_kernel(PrefillArgs a) {
 
 hipError_t launch_prefill(int layer_type, const PrefillArgs& a, hipStream_t stream) {
   const int blocks = a.nqb * a.batch * kKvHeads;
-  const size_t chunks = (size_t)a.batch * a.seq_len * kKvHeads * 32;
-  const dim3 rope_grid((unsigned)((chunks + 255) / 256));
+  const dim3 rope_grid((unsigned)(((size_t)a.seq_len * kKvHeads * 32 + 255) / 256), (unsigned)a.batch);
   if (layer_type == kSliding) {
     hipLaunchKernelGGL(prefill_rope_kernel<kSliding>, rope_grid, dim3(256), 0, stream, a);
     if (a.start_pos > 0)
@@ -588,7 +604,7 @@ hipError_t launch_prefill(int layer_type, const PrefillArgs& a, hipStream_t stre
 }
 
 size_t prefill_workspace_bytes(int batch, int seq_len) {
-  return (size_t)batch * seq_len * kKvHeads * kHeadDim * sizeof(uint16_t);
+  return (size_t)batch * seq_len * kKvHeads * kHeadDim * sizeof(uint16_t);   // [T, 4, 256] bf16
 }
 
 int prefill_block_rows() { return kBM; }

@@ -8,18 +8,20 @@
 namespace spark {
 
 struct PrefillArgs {
-  const uint16_t* q;      // [B, S, 16, 256]
-  const uint16_t* k;      // [B, S, 4, 256]
-  const uint16_t* v;      // [B, S, 4, 256]
-  uint16_t* k_rot;        // [B, S, 4, 256] workspace: K after RoPE
-  const uint16_t* gate;   // [B, S, 16]
-  uint16_t* out;          // [B, S, 16, 256]
+  const uint16_t* q;      // [T, 16, 256]: T = B * S tokens, or the sum of the lengths (varlen)
+  const uint16_t* k;      // [T, 4, 256]
+  const uint16_t* v;      // [T, 4, 256]
+  uint16_t* k_rot;        // [T, 4, 256] workspace: K after RoPE
+  const uint16_t* gate;   // [T, 16]
+  uint16_t* out;          // [T, 16, 256]
   uint16_t* cache_k;      // [B, cap, 4, 256] or null
   uint16_t* cache_v;
+  const int32_t* cu_seqlens;  // [B + 1] token offsets of the sequences (varlen), or null
+  int total_tokens;       // T
   int batch;
-  int seq_len;
+  int seq_len;            // S, or the largest length (varlen)
   int cache_cap;
-  int nqb;                // query blocks per sequence
+  int nqb;                // query blocks per sequence (of the largest)
   int start_pos;          // position of the chunk's first token; > 0: prefix in the cache
 };
 

@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define SPARK_ATTN_ABI_VERSION 5
+#define SPARK_ATTN_ABI_VERSION 6
 
 enum { SPARK_Q_HEADS = 16, SPARK_KV_HEADS = 4, SPARK_HEAD_DIM = 256, SPARK_WINDOW = 512 };
 
@@ -115,6 +115,35 @@ spark_status spark_attn_prefill(int32_t layer_type, int32_t batch, int32_t seq_l
                                 const void* v, const void* gate_logits,
                                 const spark_kv_cache* cache, void* workspace,
                                 size_t workspace_bytes, void* out, void* stream);
+
+/* Bytes of device workspace spark_attn_prefill_varlen needs: bf16 [total_tokens, 4, 256]. */
+size_t spark_attn_prefill_varlen_workspace_bytes(int32_t layer_type, int32_t total_tokens);
+
+/*
+ * Prefill of a batch of sequences of different lengths, packed one after another
+ * (variable-length batch): sequence b owns token rows cu_seqlens[b] .. cu_seqlens[b+1]-1
+ * and its token t sits at position t; each sequence attends only to itself.
+ *   cu_seqlens   device int32 [batch + 1]: 0 = cu[0] <= cu[1] <= ... <= cu[batch] =
+ *                total_tokens, every length <= max_seqlen (zero lengths allowed).  The
+ *                host cannot check device contents: a table that breaks these rules gives
+ *                unspecified outputs for the rows concerned, but every access stays inside
+ *                the buffers (the kernels clamp each sequence to [0, total_tokens) and to
+ *                max_seqlen rows).
+ *   q, out       bf16 [total_tokens, 16, 256];  k, v  bf16 [total_tokens, 4, 256], k
+ *                before RoPE;  gate_logits  bf16 [total_tokens, 16]
+ *   cache        optional, as for spark_attn_prefill with start_pos = 0 (row b receives
+ *                sequence b's rotated keys and values); FULL needs capacity >= max_seqlen
+ *   workspace    >= spark_attn_prefill_varlen_workspace_bytes(layer_type, total_tokens),
+ *                256-byte aligned
+ * 1 <= batch <= 65535, 1 <= max_seqlen <= 2^20, batch * max_seqlen < 2^32,
+ * total_tokens >= 1.  The launches and the per-row arithmetic are spark_attn_prefill's:
+ * a sequence's outputs are bit for bit those of a batch-1 call on that sequence.
+ */
+spark_status spark_attn_prefill_varlen(int32_t layer_type, int32_t batch, const int32_t* cu_seqlens,
+                                       int32_t total_tokens, int32_t max_seqlen, const void* q,
+                                       const void* k, const void* v, const void* gate_logits,
+                                       const spark_kv_cache* cache, void* workspace,
+                                       size_t workspace_bytes, void* out, void* stream);
 
 /*
  * Append `n_new` tokens per sequence to a layer's cache.

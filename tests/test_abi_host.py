@@ -30,7 +30,7 @@ def test_exports_every_declared_function():
 
 
 def test_version_and_status_strings():
-    assert fga.abi_version() == 5
+    assert fga.abi_version() == 6
     assert fga.status_string(0) == "ok"
     assert fga.status_string(3) == "workspace too small"
     assert fga.status_string(99) == "unknown status"
@@ -149,3 +149,27 @@ def test_workspace_planning_q8():
     assert ws(1, 64, 32768) == _layout_bytes(64, 512)     # two partitions per CU (256 on the host)
     assert ws(0, 1, 100000) == _layout_bytes(1, 16)       # never more than the chunks
     assert ws(2, 1, 64) == 0 and ws(1, 1, 64, -1) == 0
+
+
+def varlen(**kw):
+    a = dict(lt=1, B=2, cu=FAKE, T=100, M=64, q=FAKE, k=FAKE, v=FAKE, g=FAKE, cache=None, ws=FAKE,
+             ws_bytes=1 << 30, out=FAKE)
+    a.update(kw)
+    return lib.spark_attn_prefill_varlen(a["lt"], a["B"], a["cu"], a["T"], a["M"], a["q"], a["k"], a["v"],
+                                         a["g"], a["cache"], a["ws"], a["ws_bytes"], a["out"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(lt=2), 1), (dict(B=0), 1), (dict(M=0), 1), (dict(M=(1 << 20) + 1), 1), (dict(T=0), 1),
+    (dict(cu=None), 1), (dict(cu=ctypes.c_void_p(0x10002)), 1), (dict(q=None), 1), (dict(k=MISALIGNED), 1),
+    (dict(B=65535, M=1 << 20), 1),                 # batch * max_seqlen >= 2^32
+    (dict(cache=_cache(batch=3)), 1), (dict(cache=_cache(cap=63)), 1), (dict(lt=0, cache=_cache(cap=100)), 1),
+    (dict(ws=MISALIGNED), 1), (dict(ws_bytes=100 * 4 * 256 * 2 - 1), 3),
+])
+def test_prefill_varlen_rejects(kw, status):
+    assert varlen(**kw) == status
+
+
+def test_prefill_varlen_workspace():
+    assert fga.prefill_varlen_workspace_bytes(1, 100) == 100 * 4 * 256 * 2
+    assert fga.prefill_varlen_workspace_bytes(2, 100) == 0 and fga.prefill_varlen_workspace_bytes(0, 0) == 0
