@@ -34,6 +34,11 @@ spark_status check_cache_q8(int32_t lt, const spark_kv_cache_q8* c, int32_t batc
 
 spark_status from_hip(hipError_t e) { return e == hipSuccess ? SPARK_OK : SPARK_ERR_HIP; }
 
+// Varlen workspace: the rotated keys, then (256-byte aligned) the work-queue counter.
+size_t varlen_queue_offset(int32_t total_tokens) {
+  return (spark::prefill_workspace_bytes(1, total_tokens) + 255) & ~(size_t)255;
+}
+
 // Checks shared by spark_attn_decode and spark_attn_decode_q8 (everything but the cache).
 spark_status check_decode(int32_t layer_type, int32_t batch, const void* q, const void* gate_logits,
                           const int32_t* seq_lens, int32_t max_seq_len, int32_t num_parts,
@@ -138,7 +143,7 @@ spark_status spark_attn_prefill(int32_t layer_type, int32_t batch, int32_t seq_l
 
 size_t spark_attn_prefill_varlen_workspace_bytes(int32_t layer_type, int32_t total_tokens) {
   if (!valid_type(layer_type) || total_tokens < 1) return 0;
-  return spark::prefill_workspace_bytes(1, total_tokens);
+  return varlen_queue_offset(total_tokens) + 256;
 }
 
 spark_status spark_attn_prefill_varlen(int32_t layer_type, int32_t batch, const int32_t* cu_seqlens,
@@ -161,7 +166,7 @@ spark_status spark_attn_prefill_varlen(int32_t layer_type, int32_t batch, const 
     if (layer_type == SPARK_LAYER_FULL && cache->capacity < max_seqlen) return SPARK_ERR_INVALID_ARG;
   }
   if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u)) return SPARK_ERR_INVALID_ARG;
-  if (workspace_bytes < spark::prefill_workspace_bytes(1, total_tokens)) return SPARK_ERR_WORKSPACE;
+  if (workspace_bytes < varlen_queue_offset(total_tokens) + 256) return SPARK_ERR_WORKSPACE;
   const int rows = spark::prefill_block_rows();
 
   spark::PrefillArgs a{};
@@ -174,6 +179,7 @@ spark_status spark_attn_prefill_varlen(int32_t layer_type, int32_t batch, const 
   a.cache_k = cache ? static_cast<uint16_t*>(cache->k) : nullptr;
   a.cache_v = cache ? static_cast<uint16_t*>(cache->v) : nullptr;
   a.cu_seqlens = cu_seqlens;
+  a.sched = reinterpret_cast<int*>(static_cast<char*>(workspace) + varlen_queue_offset(total_tokens));
   a.total_tokens = total_tokens;
   a.batch = batch;
   a.seq_len = max_seqlen;

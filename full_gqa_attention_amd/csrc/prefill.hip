@@ -212,6 +212,8 @@ __global__ __launch_bounds__(256) void prefill_rope_kernel(PrefillArgs a) {
   __shared__ double s_inv[T::kRot / 2];
   if (threadIdx.x < T::kRot / 2) s_inv[threadIdx.x] = rope_inv_rev(threadIdx.x, T::kRot, log2(T::kTheta));
   __syncthreads();
+  // The attention launch that follows claims its work from this counter (varlen).
+  if (a.sched != nullptr && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *a.sched = 0;
   // Grid: x = tokens of a sequence (two per workgroup), y = sequence.
   const int b = blockIdx.y;
   const SeqSpan sp = seq_span(a, b);
@@ -357,11 +359,39 @@ void prefill_kernel(PrefillArgs a) {
   const int P = PFX ? a.start_pos : 0;      // position of chunk row 0
 
   int b, g, qb;
-  block_coords<LT>(blockIdx.x, a.batch, a.nqb, b, g, qb);
+  if (PFX || a.sched == nullptr) {        // prefix calls are never varlen
+    block_coords<LT>(blockIdx.x, a.batch, a.nqb, b, g, qb);
+  } else {
+    // Variable lengths: workgroups go to the XCDs round-robin by id, so a fixed mapping would
+    // give some XCDs more work than others.  Instead each workgroup claims the next item of
+    // one queue, in the order the fixed mapping would use (latest blocks first on full
+    // layers), skipping blocks past the end of their sequence; the grid has one workgroup
+    // per item, so every item is claimed once.
+    __shared__ int s_item;
+    if (tid == 0) {
+      const int units = a.batch * kKvHeads, items = units * a.nqb;
+      int item = -1;
+      for (;;) {
+        const int k = atomicAdd(a.sched, 1);
+        if (k >= items) break;
+        const int qx = k / units, qbk = (LT == kFull) ? (a.nqb - 1 - qx) : qx;
+        if (qbk * kBM < seq_span(a, (k % units) / kKvHeads).len) { item = k; break; }
+      }
+      s_item = item;
+    }
+    __syncthreads();
+    const int item = s_item;
+    if (item < 0) return;                   // the queue ran out (whole workgroup)
+    const int units = a.batch * kKvHeads;
+    b = (item % units) / kKvHeads;
+    g = item % kKvHeads;
+    const int qx = item / units;
+    qb = (LT == kFull) ? (a.nqb - 1 - qx) : qx;
+  }
   const int q0 = qb * kBM;
   const SeqSpan sp = seq_span(a, b);
   const int S = sp.len;                     // chunk rows of this sequence
-  if (q0 >= S) return;                      // varlen: a shorter sequence (whole workgroup)
+  if (q0 >= S) return;                      // a shorter sequence (whole workgroup)
   const int hq = g * kGroup + (kRowBlocks == 2 ? wave : wave >> 1);
   const int rb0 = kRowBlocks == 2 ? 0 : (wave & 1);      // first 32-row block of this wave
 

@@ -17,6 +17,7 @@ struct PrefillArgs {
   uint16_t* cache_k;      // [B, cap, 4, 256] or null
   uint16_t* cache_v;
   const int32_t* cu_seqlens;  // [B + 1] token offsets of the sequences (varlen), or null
+  int* sched;             // varlen: work-queue counter in the workspace (zeroed by the RoPE pass)
   int total_tokens;       // T
   int batch;
   int seq_len;            // S, or the largest length (varlen)

@@ -116,7 +116,8 @@ spark_status spark_attn_prefill(int32_t layer_type, int32_t batch, int32_t seq_l
                                 const spark_kv_cache* cache, void* workspace,
                                 size_t workspace_bytes, void* out, void* stream);
 
-/* Bytes of device workspace spark_attn_prefill_varlen needs: bf16 [total_tokens, 4, 256]. */
+/* Bytes of device workspace spark_attn_prefill_varlen needs: bf16 [total_tokens, 4, 256],
+ * then (256-byte aligned) a 256-byte block holding the work queue of the attention launch. */
 size_t spark_attn_prefill_varlen_workspace_bytes(int32_t layer_type, int32_t total_tokens);
 
 /*
@@ -136,8 +137,11 @@ size_t spark_attn_prefill_varlen_workspace_bytes(int32_t layer_type, int32_t tot
  *   workspace    >= spark_attn_prefill_varlen_workspace_bytes(layer_type, total_tokens),
  *                256-byte aligned
  * 1 <= batch <= 65535, 1 <= max_seqlen <= 2^20, batch * max_seqlen < 2^32,
- * total_tokens >= 1.  The launches and the per-row arithmetic are spark_attn_prefill's:
- * a sequence's outputs are bit for bit those of a batch-1 call on that sequence.
+ * total_tokens >= 1.  The per-row arithmetic is spark_attn_prefill's: a sequence's
+ * outputs are bit for bit those of a batch-1 call on that sequence.  The attention
+ * workgroups take their query blocks from a queue in the workspace (latest blocks first on
+ * FULL layers), which the RoPE launch resets, so that unequal lengths still spread evenly
+ * over the XCDs; calls sharing a workspace must be ordered on a stream.
  */
 spark_status spark_attn_prefill_varlen(int32_t layer_type, int32_t batch, const int32_t* cu_seqlens,
                                        int32_t total_tokens, int32_t max_seqlen, const void* q,

@@ -164,12 +164,12 @@ def varlen(**kw):
     (dict(cu=None), 1), (dict(cu=ctypes.c_void_p(0x10002)), 1), (dict(q=None), 1), (dict(k=MISALIGNED), 1),
     (dict(B=65535, M=1 << 20), 1),                 # batch * max_seqlen >= 2^32
     (dict(cache=_cache(batch=3)), 1), (dict(cache=_cache(cap=63)), 1), (dict(lt=0, cache=_cache(cap=100)), 1),
-    (dict(ws=MISALIGNED), 1), (dict(ws_bytes=100 * 4 * 256 * 2 - 1), 3),
+    (dict(ws=MISALIGNED), 1), (dict(ws_bytes=100 * 4 * 256 * 2 + 255), 3),
 ])
 def test_prefill_varlen_rejects(kw, status):
     assert varlen(**kw) == status
 
 
 def test_prefill_varlen_workspace():
-    assert fga.prefill_varlen_workspace_bytes(1, 100) == 100 * 4 * 256 * 2
+    assert fga.prefill_varlen_workspace_bytes(1, 100) == 100 * 4 * 256 * 2 + 256
     assert fga.prefill_varlen_workspace_bytes(2, 100) == 0 and fga.prefill_varlen_workspace_bytes(0, 0) == 0
