@@ -132,7 +132,8 @@ def sliding_pairs(S):
 def bench_configs(fga, synth):
     """The other workloads of the hot path's scope table, each timed on its own:
     sliding prefill S=1024; a chunk of 8192 after a cached prefix of 8192 (both layer
-    types); the 36-layer stack at S=32768; decode over the 8-bit cache; batched decode (full, cold
+    types); a variable-length batch of 16 sequences; the 36-layer stack at S=32768; decode
+    over the 8-bit cache; one decode step of all 36 layers (bf16 and 8-bit caches); batched decode (full, cold
     caches; sliding ring, warm and cold); long decode at 128K and 1M tokens."""
     import numpy as np
     import torch
@@ -172,6 +173,25 @@ def bench_configs(fga, synth):
         log(f"chunked prefill {name} P=8192 n=8192: {ms:.3f} ms  {tf:.0f} TFLOP/s")
         del cache, ws
     del q, k, v, g, o
+
+    # Variable-length batch: 16 sequences of lengths uniform in [512, 8192], packed.
+    lens = np.random.default_rng(synth.CONFIG_SEED[2] + 200).integers(512, 8193, size=16)
+    T = int(lens.sum())
+    cu = torch.as_tensor(np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)).cuda()
+    gen.manual_seed(synth.CONFIG_SEED[2] + 201)
+    q, k, v, g = (dev_normal(gen, (T, 16, 256)), dev_normal(gen, (T, 4, 256)),
+                  dev_normal(gen, (T, 4, 256)), dev_normal(gen, (T, 16)))
+    o = torch.empty_like(q)
+    ws = torch.empty(fga.prefill_varlen_workspace_bytes(fga.FULL, T), dtype=torch.uint8, device="cuda")
+    for lt, name in ((fga.FULL, "full"), (fga.SLIDING, "sliding")):
+        ms = time_launches(lambda: fga.prefill_varlen(lt, q, k, v, g, cu, int(lens.max()), out=o, workspace=ws),
+                           50, 10)
+        pairs = int(sum(n * (n + 1) // 2 for n in lens)) if lt == fga.FULL else int(sum(sliding_pairs(int(n)) for n in lens))
+        tf = 16384 * pairs / (ms * 1e-3) / 1e12
+        out[f"varlen_prefill_{name}_16seq"] = {"ms": ms, "tflops": tf, "frac_mfma": tf / PEAK_BF16_TFLOPS,
+                                               "tokens_per_s": T / (ms * 1e-3), "tokens": T}
+        log(f"varlen prefill {name}, 16 sequences (T={T}): {ms:.3f} ms  {tf:.0f} TFLOP/s")
+    del q, k, v, g, o, ws, cu
 
     # Config 4: 36-layer stack, batch 1, S = 32768, independent inputs per layer (drawn on
     # the device: 24 GB of N(0,1) bf16); layer l is full iff l % 4 == 3.
@@ -279,8 +299,50 @@ def bench_configs(fga, synth):
         out[f"decode_q8_full_b{B}_l{L}_cold"] = r
         log(f"config 5 decode q8 full B={B} L={L}, cold: {r['us']:.0f} us  {r['gbs']:.0f} GB/s")
         torch.cuda.empty_cache()
+    # One decode step of the whole 36-layer model: batch 64, lengths uniform in [1024, 32768]
+    # (each layer its own cache: 9 full caches, 27 rings), bf16 and 8-bit caches.
     del flush_a
     torch.cuda.empty_cache()
+    seed = synth.CONFIG_SEED[3]
+    lens = synth.decode_seq_lens(seed, 64, 1024, 32768)
+    sl = torch.as_tensor(lens).cuda()
+    maxlen = int(lens.max())
+    B = 64
+    for kv in ("bf16", "q8_0"):
+        gen.manual_seed(seed + 300)
+        layers = []
+        for layer in range(36):
+            lt = fga.FULL if layer % 4 == 3 else fga.SLIDING
+            cap = maxlen if lt == fga.FULL else 512
+            if kv == "bf16":
+                cache = fga.KVCache(lt, B, cap, k=dev_normal(gen, (B, cap, 4, 256)), v=dev_normal(gen, (B, cap, 4, 256)))
+                wsb = fga.decode_workspace_bytes(lt, B, maxlen)
+            else:
+                codes = lambda: torch.randint(-127, 128, (B, cap, 4, 256), generator=gen, device="cuda", dtype=torch.int8)
+                scales = lambda: (0.005 + 0.025 * torch.rand((B, cap, 4, 8), generator=gen, device="cuda")).half()
+                cache = fga.KVCacheQ8(lt, B, cap, k=codes(), k_scale=scales(), v=codes(), v_scale=scales())
+                wsb = fga.decode_q8_workspace_bytes(lt, B, maxlen)
+            layers.append((lt, cache, dev_normal(gen, (B, 16, 256)), dev_normal(gen, (B, 16)),
+                           torch.empty(wsb, dtype=torch.uint8, device="cuda"),
+                           torch.empty(B, 16, 256, dtype=torch.bfloat16, device="cuda")))
+        dec = fga.decode if kv == "bf16" else fga.decode_q8
+
+        def step():
+            for lt, cache, qd, gd, wsd, od in layers:
+                dec(lt, qd, gd, cache, sl, maxlen, out=od, workspace=wsd)
+
+        ms = time_launches(step, 10, 3)
+        vis = int(lens.astype(np.int64).sum()) * 9 + int(np.minimum(lens, 512).astype(np.int64).sum()) * 27
+        row = 2 * 4 * (512 if kv == "bf16" else 272)
+        nbytes = vis * row + 36 * B * (16 * 256 * 4 + 32)
+        out[f"decode_step_36_layers_b64_{kv}"] = {"ms": ms, "tokens_per_s": B / (ms * 1e-3),
+                                                  "gbs": nbytes / (ms * 1e-3) / 1e9,
+                                                  "frac_hbm": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                                                  "bytes": nbytes, "kv": kv}
+        log(f"36-layer decode step, batch 64 ({kv} cache): {ms:.2f} ms  {B / (ms * 1e-3):.0f} tokens/s  "
+            f"{nbytes / (ms * 1e-3) / 1e9:.0f} GB/s")
+        del layers
+        torch.cuda.empty_cache()
     return out
 
 
