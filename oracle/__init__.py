@@ -12,6 +12,10 @@ Pages cited (titles as given by their addresses):
   [HYB]   Spark-X2.6-4B-Base hybrid attention explainer (eliteato.com/news/34565)
   [GGUF]  Sharp-Spark-X2.5-4B-GGUF on a 6 GB GPU (mpbf.cn/news/67460)
 
+Modules: ``attention`` (prefill, chunked and varlen prefill, append, decode), ``kvq8``
+(the 8-bit q8_0 cache), ``proj`` (the W8A8 FP8 q_k_v_proj and the bf16 g_proj that feed
+the path), ``footprint`` (KV byte counts).
+
 Pinning status: every function is pinned by ``tests/test_oracle_*.py`` (closed forms,
 invariants, brute force, a library cross-check and the pages' KV-size figures); the
 8-bit cache (``kvq8``) by exact closed forms of the q8_0 rule, its error bound, and the
@@ -51,6 +55,12 @@ from .kvq8 import (  # noqa: F401
     kv_append_q8,
     q8_dequantize,
     q8_quantize,
+)
+from .proj import (  # noqa: F401
+    e4m3fn_decode,
+    e4m3fn_encode,
+    qkv_proj,
+    quantize_tokens,
 )
 from .footprint import (  # noqa: F401
     kv_bytes_full_layer_per_token,

@@ -153,3 +153,40 @@ def q8_cache_rows(seed: int, b: int, n: int) -> tuple:
             fp16_scales(seed, 101 + 4 * b, (n, N_KV_HEADS, HEAD_DIM // 32)),
             int8_codes(seed, 102 + 4 * b, (n, N_KV_HEADS, HEAD_DIM)),
             fp16_scales(seed, 103 + 4 * b, (n, N_KV_HEADS, HEAD_DIM // 32)))
+
+
+def normal_bf16_scaled(seed: int, tensor_index: int, shape, log2_scale: int) -> np.ndarray:
+    """As normal_bf16, with every value multiplied by 2**log2_scale before rounding."""
+    shape = tuple(int(s) for s in shape)
+    vals = bf16_bits_to_f32(normal_bf16(seed, tensor_index, shape)) * np.float32(2.0 ** log2_scale)
+    return f32_to_bf16_bits(vals)
+
+
+def fp8_e4m3_codes(seed: int, tensor_index: int, shape, exp_lo: int = -3, exp_hi: int = 3) -> np.ndarray:
+    """Random FP8 E4M3 (OCP, bias 7) codes: uniform sign, exponent uniform in
+    [exp_lo, exp_hi], uniform 3-bit mantissa -- finite normal values of magnitude
+    2^exp_lo .. 2^(exp_hi+1) (synthetic quantised weights)."""
+    shape = tuple(int(s) for s in shape)
+    rng = np.random.default_rng(np.random.SeedSequence(seed, spawn_key=(tensor_index, 0)))
+    sign = rng.integers(0, 2, size=shape) << 7
+    e = rng.integers(exp_lo, exp_hi + 1, size=shape) + 7
+    m = rng.integers(0, 8, size=shape)
+    return (sign | (e << 3) | m).astype(np.uint8)
+
+
+def uniform_f32(seed: int, tensor_index: int, shape, lo: float, hi: float) -> np.ndarray:
+    """Uniform float32 values in [lo, hi) (e.g. per-channel weight scales)."""
+    rng = np.random.default_rng(np.random.SeedSequence(seed, spawn_key=(tensor_index, 0)))
+    return rng.uniform(lo, hi, size=tuple(int(s) for s in shape)).astype(np.float32)
+
+
+def proj_inputs(seed: int, tokens: int) -> dict:
+    """Hidden states x [T, 2560] bf16 N(0,1); q_k_v_proj weights as E4M3 codes
+    [6144, 2560] with per-channel scales in [0.003, 0.007) (outputs of order 1); g_proj
+    weights [16, 2560] bf16 N(0, 2^-12) (gate logits of order 1)."""
+    return {
+        "x": normal_bf16(seed, 0, (tokens, 2560)),
+        "w": fp8_e4m3_codes(seed, 1, (6144, 2560)),
+        "w_scale": uniform_f32(seed, 2, (6144,), 0.003, 0.007),
+        "wg": normal_bf16_scaled(seed, 3, (16, 2560), -6),
+    }

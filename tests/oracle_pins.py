@@ -649,6 +649,90 @@ Q8_PINS = [pin_q8_closed_form, pin_q8_zero_and_half_away, pin_q8_error_bound]
 Q8_ATT_PINS = [pin_kv_append_q8, pin_decode_q8]
 
 
+# --------------------------------------------------------------------------- FP8 projections
+
+
+def pin_e4m3fn_codec(pj):
+    """OCP E4M3FN: closed-form codes, every finite code round-trips, ties go to the even
+    mantissa, the spacing is 2^(e-3), 448 is the largest finite value."""
+    cases = {1.0: 0x38, -1.0: 0xB8, 0.5: 0x30, 2.0: 0x40, -2.0: 0xC0, 448.0: 0x7E, -448.0: 0xFE,
+             2.0 ** -9: 0x01, 2.0 ** -6: 0x08, 7 * 2.0 ** -9: 0x07, 240.0: 0x77, 0.0: 0x00, 1.75: 0x3E,
+             1.0625: 0x38, 1.1875: 0x3A, 3 * 2.0 ** -10: 0x02, 2.0 ** -10: 0x00, 460.0: 0x7E, 17.0: 0x58, 18.0: 0x59}
+    got = pj.e4m3fn_encode(list(cases))
+    assert got.tolist() == list(cases.values()), [hex(int(x)) for x in got]
+    codes = np.arange(256, dtype=np.uint8)
+    finite = codes[(codes & 0x7F) != 0x7F]
+    assert np.array_equal(pj.e4m3fn_encode(pj.e4m3fn_decode(finite)), finite)
+    pos = pj.e4m3fn_decode(np.arange(0x7F, dtype=np.uint8))
+    assert (np.diff(pos) > 0).all() and pos[-1] == 448.0
+    for c in range(0x08, 0x7E):                            # normal codes: spacing 2^(e-3)
+        e = (c >> 3) - 7
+        assert pos[c + 1] - pos[c] == 2.0 ** (e - 3) or (c & 7) == 7
+    assert np.isnan(pj.e4m3fn_decode([0x7F, 0xFF])).all()
+    assert pj.e4m3fn_encode([464.0])[0] == 0x7E          # the tie rounds to the even 448
+    for bad in (464.5, 1e6):
+        try:
+            pj.e4m3fn_encode([bad])
+        except ValueError:
+            continue
+        raise AssertionError(f"{bad} should not encode")
+
+
+def _bf16(att, x):
+    return att.round_to_bf16_bits(np.asarray(x, dtype=np.float64))
+
+
+def pin_token_quantizer(att, pj):
+    """Per-token scales: max |x| codes to +-448, values read back within half a step
+    (2^-4 relative for normals, s 2^-10 absolute below), sign symmetric; a zero row has
+    scale 0 and codes 0."""
+    rng = np.random.default_rng(71)
+    x = np.concatenate([rng.standard_normal((6, 2560)), 1e-3 * rng.standard_cauchy((2, 2560)),
+                        np.zeros((1, 2560))])
+    xb = _bf16(att, x)
+    codes, s = pj.quantize_tokens(xb)
+    xv = att.bf16_to_f64(xb)
+    assert codes.shape == (9, 2560) and s.dtype == np.float32 and s[-1] == 0 and not codes[-1].any()
+    top = np.abs(pj.e4m3fn_decode(codes[np.arange(8), np.argmax(np.abs(xv[:8]), axis=1)]))
+    assert (top == 448.0).all()
+    back = pj.e4m3fn_decode(codes[:8]) * s[:8, None]
+    err = np.abs(back - xv[:8])
+    assert (err <= np.abs(xv[:8]) / 16 + s[:8, None] * 2.0 ** -10 + 1e-12).all()
+    nc, ns = pj.quantize_tokens(_bf16(att, -x))
+    assert np.array_equal(ns, s) and np.array_equal(nc[:8] ^ 0x80, codes[:8]) or \
+        np.array_equal(pj.e4m3fn_decode(nc), -pj.e4m3fn_decode(codes))
+
+
+def pin_qkv_proj_identity(att, pj):
+    """Identity-like weights (channel n reads input n mod 2560 with code 1.0, scale 1)
+    return the quantised activations, in the q/k/v split and head layout; one-hot gate
+    rows return the chosen inputs exactly; scales act linearly."""
+    rng = np.random.default_rng(72)
+    T = 5
+    xb = _bf16(att, rng.standard_normal((T, 2560)))
+    w = np.zeros((6144, 2560), np.uint8)
+    w[np.arange(6144), np.arange(6144) % 2560] = 0x38
+    ws = np.ones(6144, np.float32)
+    pick = rng.choice(2560, 16, replace=False)
+    wg = np.zeros((16, 2560), np.uint16)
+    wg[np.arange(16), pick] = 0x3F80                     # bf16 1.0
+    q, k, v, g = pj.qkv_proj(xb, w, ws, wg)
+    codes, s = pj.quantize_tokens(xb)
+    xq = pj.e4m3fn_decode(codes) * s[:, None]
+    full = xq[:, np.arange(6144) % 2560]
+    _close(q, full[:, :4096].reshape(T, 16, 256), 1e-12, "q")
+    _close(q[:, 3, 7], xq[:, 3 * 256 + 7], 1e-12, "q head 3 dim 7")
+    _close(k, full[:, 4096:5120].reshape(T, 4, 256), 1e-12, "k")
+    _close(v[:, 2, 5], xq[:, (5120 + 2 * 256 + 5) % 2560], 1e-12, "v head 2 dim 5")
+    _close(g, att.bf16_to_f64(xb)[:, pick], 0.0, "gate one-hot")
+    q2, _, v2, _ = pj.qkv_proj(xb, w, 2 * ws, wg)
+    _close(q2, 2 * q, 1e-12, "linear in the channel scale")
+
+
+PROJ_PINS = [pin_e4m3fn_codec]
+PROJ_ATT_PINS = [pin_token_quantizer, pin_qkv_proj_identity]
+
+
 ALL_PINS = [
     pin_brute_force_tiny, pin_brute_force_real_heads, pin_window_covering_sequence_is_causal,
     pin_window_one_closed_form, pin_row_zero_closed_form, pin_constant_values,

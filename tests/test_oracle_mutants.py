@@ -94,3 +94,33 @@ def test_planted_q8_mistake_is_caught(name):
             caught.append(pin.__name__)
             break
     assert caught, f"no pin fails for the planted mistake {name}"
+
+
+PROJ_SRC = os.path.join(os.path.dirname(SRC), "proj.py")
+PROJ_MUTANTS = {
+    "e4m3_bias_8": ("np.ldexp(1.0 + m / 8.0, e - 7)", "np.ldexp(1.0 + m / 8.0, e - 8)"),
+    "e4m3_round_half_up": ("q = np.rint(a / step)", "q = np.floor(a / step + 0.5)"),
+    "token_scale_range_240": ("amax / np.float32(E4M3_MAX)", "amax / np.float32(240.0)"),
+    "kv_split_swapped": ("y[:, 4096:5120].reshape(T, 4, 256),\n            y[:, 5120:].reshape(T, 4, 256)",
+                         "y[:, 5120:].reshape(T, 4, 256),\n            y[:, 4096:5120].reshape(T, 4, 256)"),
+    "gate_from_quantised_x": ("gate = bf16_to_f64(x_bits) @", "gate = (e4m3fn_decode(xc) * xs[:, None]) @"),
+    "channel_scale_dropped": (" * np.asarray(w_scales, dtype=np.float64)[None, :]", ""),
+}
+
+
+@pytest.mark.parametrize("name", sorted(PROJ_MUTANTS))
+def test_planted_proj_mistake_is_caught(name):
+    import oracle.attention as att
+    old, new = PROJ_MUTANTS[name]
+    src = open(PROJ_SRC).read()
+    assert src.count(old) == 1, f"mutation site must occur exactly once: {old!r}"
+    mod = types.ModuleType("oracle_proj_mutant")
+    exec(compile(src.replace(old, new), "oracle_proj_mutant", "exec"), mod.__dict__)
+    caught = []
+    for pin in P.PROJ_PINS + P.PROJ_ATT_PINS:
+        try:
+            pin(mod) if pin in P.PROJ_PINS else pin(att, mod)
+        except (AssertionError, IndexError, ValueError):
+            caught.append(pin.__name__)
+            break
+    assert caught, f"no pin fails for the planted mistake {name}"

@@ -5,6 +5,7 @@ import pytest
 import oracle.attention as att
 import oracle.footprint as fp
 import oracle.kvq8 as q8
+import oracle.proj as pj
 import oracle_pins as P
 
 
@@ -29,3 +30,13 @@ def test_q8_att_pin(pin):
 
 def test_q8_row_bytes():
     P.pin_q8_row_bytes(q8, fp)
+
+
+@pytest.mark.parametrize("pin", P.PROJ_PINS, ids=lambda f: f.__name__)
+def test_proj_pin(pin):
+    pin(pj)
+
+
+@pytest.mark.parametrize("pin", P.PROJ_ATT_PINS, ids=lambda f: f.__name__)
+def test_proj_att_pin(pin):
+    pin(att, pj)
