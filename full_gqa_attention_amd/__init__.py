@@ -60,6 +60,10 @@ def _load():
     lib.spark_attn_prefill_varlen_workspace_bytes.restype = sz
     lib.spark_attn_prefill_varlen.argtypes = [i32, i32, vp, i32, i32, vp, vp, vp, vp, cache_p, vp, sz, vp, vp]
     lib.spark_attn_prefill_varlen.restype = i32
+    lib.spark_qkv_proj_fp8_workspace_bytes.argtypes = [i32]
+    lib.spark_qkv_proj_fp8_workspace_bytes.restype = sz
+    lib.spark_qkv_proj_fp8.argtypes = [i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.spark_qkv_proj_fp8.restype = i32
     lib.spark_kv_append.argtypes = [i32, i32, i32, vp, vp, vp, cache_p, vp]
     lib.spark_kv_append.restype = i32
     lib.spark_attn_decode_workspace_bytes.argtypes = [i32, i32, i32, i32]
@@ -84,7 +88,8 @@ _lib = _load()
 
 LIBRARY_PATH = _LIB_PATH
 EXPORTED = ("spark_attn_prefill_workspace_bytes", "spark_attn_prefill", "spark_attn_prefill_varlen_workspace_bytes",
-            "spark_attn_prefill_varlen", "spark_kv_append", "spark_attn_decode_workspace_bytes",
+            "spark_attn_prefill_varlen", "spark_qkv_proj_fp8_workspace_bytes", "spark_qkv_proj_fp8",
+            "spark_kv_append", "spark_attn_decode_workspace_bytes",
             "spark_attn_decode", "spark_kv_append_q8", "spark_attn_decode_q8_workspace_bytes", "spark_attn_decode_q8", "spark_status_string",
             "spark_abi_version")
 
@@ -254,6 +259,40 @@ def prefill_varlen(layer_type: int, q, k, v, gate, cu_seqlens, max_seqlen: int, 
     if st:
         raise SparkError(st, "spark_attn_prefill_varlen")
     return out
+
+
+def qkv_proj_fp8_workspace_bytes(tokens: int) -> int:
+    return int(_lib.spark_qkv_proj_fp8_workspace_bytes(int(tokens)))
+
+
+def qkv_proj_fp8(x, w_qkv, w_scale, w_gate, out=None, workspace=None, stream=None):
+    """spark_qkv_proj_fp8: x [T,2560] bf16; w_qkv [6144,2560] uint8 E4M3FN codes; w_scale
+    [6144] fp32; w_gate [16,2560] bf16.  Returns (q [T,16,256], k [T,4,256], v [T,4,256],
+    gate logits [T,16]), all bf16."""
+    torch = _torch()
+    T = int(x.shape[0])
+    _check(x, "x", (T, 2560), torch.bfloat16)
+    _check(w_qkv, "w_qkv", (6144, 2560), torch.uint8)
+    _check(w_scale, "w_scale", (6144,), torch.float32)
+    _check(w_gate, "w_gate", (16, 2560), torch.bfloat16)
+    if out is None:
+        out = (torch.empty(T, N_Q_HEADS, HEAD_DIM, dtype=torch.bfloat16, device=x.device),
+               torch.empty(T, N_KV_HEADS, HEAD_DIM, dtype=torch.bfloat16, device=x.device),
+               torch.empty(T, N_KV_HEADS, HEAD_DIM, dtype=torch.bfloat16, device=x.device),
+               torch.empty(T, N_Q_HEADS, dtype=torch.bfloat16, device=x.device))
+    q, k, v, g = out
+    _check(q, "q", (T, N_Q_HEADS, HEAD_DIM), torch.bfloat16)
+    _check(k, "k", (T, N_KV_HEADS, HEAD_DIM), torch.bfloat16)
+    _check(v, "v", (T, N_KV_HEADS, HEAD_DIM), torch.bfloat16)
+    _check(g, "gate", (T, N_Q_HEADS), torch.bfloat16)
+    if workspace is None:
+        workspace = torch.empty(qkv_proj_fp8_workspace_bytes(T), dtype=torch.uint8, device=x.device)
+    _check(workspace, "workspace", None, torch.uint8)
+    st = _lib.spark_qkv_proj_fp8(T, _ptr(x), _ptr(w_qkv), _ptr(w_scale), _ptr(w_gate), _ptr(q), _ptr(k),
+                                 _ptr(v), _ptr(g), _ptr(workspace), int(workspace.numel()), _stream(stream))
+    if st:
+        raise SparkError(st, "spark_qkv_proj_fp8")
+    return q, k, v, g
 
 
 def kv_append(layer_type: int, k, v, pos, cache: KVCache, stream=None):

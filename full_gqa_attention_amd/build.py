@@ -13,7 +13,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIB_NAME = "libspark_attn.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
-SOURCES = ["abi.hip", "prefill.hip", "decode.hip", "kv_append.hip"]
+SOURCES = ["abi.hip", "prefill.hip", "decode.hip", "kv_append.hip", "proj.hip"]
 
 # Packed fp32 VALU ops are disabled: hipcc otherwise forms v_pk_* fp32 instructions on
 # its own from scalar float code.

@@ -189,6 +189,38 @@ spark_status spark_attn_prefill_varlen(int32_t layer_type, int32_t batch, const 
   return from_hip(spark::launch_prefill(layer_type, a, static_cast<hipStream_t>(stream)));
 }
 
+size_t spark_qkv_proj_fp8_workspace_bytes(int32_t tokens) {
+  if (tokens < 1 || tokens > kMaxSeq) return 0;
+  return spark::proj_workspace_bytes(tokens);
+}
+
+spark_status spark_qkv_proj_fp8(int32_t tokens, const void* x, const void* w_qkv, const float* w_scale,
+                                const void* w_gate, void* q, void* k, void* v, void* gate_logits,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  if (tokens < 1 || tokens > kMaxSeq) return SPARK_ERR_INVALID_ARG;
+  if (!x || !w_qkv || !w_scale || !w_gate || !q || !k || !v || !gate_logits || !workspace)
+    return SPARK_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(w_qkv) || !aligned16(w_gate) || !aligned16(q) || !aligned16(k) ||
+      !aligned16(v) || !aligned2(gate_logits) || (reinterpret_cast<uintptr_t>(w_scale) & 3u) ||
+      (reinterpret_cast<uintptr_t>(workspace) & 255u))
+    return SPARK_ERR_INVALID_ARG;
+  if (workspace_bytes < spark::proj_workspace_bytes(tokens)) return SPARK_ERR_WORKSPACE;
+  spark::ProjArgs a{};
+  a.x = static_cast<const uint16_t*>(x);
+  a.w = static_cast<const uint8_t*>(w_qkv);
+  a.w_scale = w_scale;
+  a.w_gate = static_cast<const uint16_t*>(w_gate);
+  a.xq = static_cast<uint8_t*>(workspace);
+  a.xs = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                  (((size_t)tokens * 2560 + 255) & ~(size_t)255));
+  a.q = static_cast<uint16_t*>(q);
+  a.k = static_cast<uint16_t*>(k);
+  a.v = static_cast<uint16_t*>(v);
+  a.gate = static_cast<uint16_t*>(gate_logits);
+  a.tokens = tokens;
+  return from_hip(spark::launch_qkv_proj(a, static_cast<hipStream_t>(stream)));
+}
+
 spark_status spark_kv_append(int32_t layer_type, int32_t batch, int32_t n_new,
                              const void* k, const void* v, const int32_t* pos,
                              const spark_kv_cache* cache, void* stream) {

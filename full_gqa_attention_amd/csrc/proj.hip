@@ -1,0 +1,238 @@
+// Upstream projections of the attention layer on gfx950, in W8A8 FP8 (Spark-X2.6-4B-FP8
+// walkthrough, nxmr.cn/news/148448, sections 二 and 三): q_k_v_proj with FP8 E4M3 weights
+// (one static scale per output channel) and activations quantised to FP8 per token with a
+// dynamic scale; g_proj in BF16.  Hidden 2560 -> q 4096, k 1024, v 1024 (section 一).
+//
+// Two launches:
+//   * quant_gate_kernel: one wave per token reads its 2560 hidden values once, computes the
+//     16 gate logits in fp32 from the bf16 values (g_proj), s = max|x| / 448 and the OCP
+//     E4M3FN codes of x / s (v_cvt_pk_fp8_f32: nearest even), into the workspace;
+//   * qkv_gemm_kernel: C = X_q W_q^T on v_mfma_scale_f32_32x32x64_f8f6f4 (block scales 1),
+//     128 x 128 output tiles, K in stages of 128 bytes through a two-stage LDS ring filled
+//     by direct global->LDS loads; epilogue C * s_token * s_channel, rounded to bf16 and
+//     stored straight into the q, k or v layout the attention path reads.
+#include "spark_device.hpp"
+#include "spark_launch.hpp"
+
+namespace spark {
+namespace {
+
+constexpr int kHidden = 2560;
+constexpr int kQkvOut = 6144;
+constexpr int kQOut = kQHeads * kHeadDim;      // 4096
+constexpr int kKvOut = kKvHeads * kHeadDim;    // 1024
+constexpr int kGates = kQHeads;                // 16 gate logits per token
+constexpr float kE4M3Max = 448.0f;
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+// ---------------------------------------------------------------------------------------
+// Quantisation of the activations and the bf16 gate projection, one wave per token.
+// Lane l holds the 16-byte chunks l + 64 i (i < 5) of the row: each load is one
+// contiguous kilobyte across the wave.
+__global__ __launch_bounds__(256) void quant_gate_kernel(ProjArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= a.tokens) return;                                   // whole wave
+  const uint16_t* xr = a.x + (size_t)t * kHidden;
+  float xv[40];
+#pragma unroll
+  for (int i = 0; i < 5; ++i) {
+    const u32x4 r = ld_global16(xr + 8 * (lane + 64 * i));
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      xv[8 * i + 2 * w] = bf16_lo(r[w]);
+      xv[8 * i + 2 * w + 1] = bf16_hi(r[w]);
+    }
+  }
+  // g_proj in bf16: 16 dot products, fp32 partial sums per lane, then across the wave.
+  float gl[kGates];
+#pragma unroll
+  for (int h = 0; h < kGates; ++h) {
+    float acc = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 5; ++i) {
+      const u32x4 r = ld_global16(a.w_gate + (size_t)h * kHidden + 8 * (lane + 64 * i));
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        acc = fmaf(xv[8 * i + 2 * w], bf16_lo(r[w]), acc);
+        acc = fmaf(xv[8 * i + 2 * w + 1], bf16_hi(r[w]), acc);
+      }
+    }
+    gl[h] = acc;
+  }
+#pragma unroll
+  for (int h = 0; h < kGates; ++h)
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) gl[h] += __shfl_xor(gl[h], off);
+  if (lane < kGates) {
+    float g = gl[0];
+#pragma unroll
+    for (int h = 1; h < kGates; ++h) g = lane == h ? gl[h] : g;
+    a.gate[(size_t)t * kGates + lane] = (uint16_t)(pack_bf16x2(g, 0.0f) & 0xffffu);
+  }
+  // Per-token FP8: s = max|x| / 448, codes E4M3FN(x / s), both divisions IEEE fp32.
+  float m = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 40; ++j) m = fmaxf(m, fabsf(xv[j]));
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+  const float s = m / kE4M3Max;
+  uint8_t* qr = a.xq + (size_t)t * kHidden;
+#pragma unroll
+  for (int i = 0; i < 5; ++i) {
+    uint32_t w[2];
+#pragma unroll
+    for (int d = 0; d < 2; ++d) {
+      float y[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) y[e] = s > 0.0f ? xv[8 * i + 4 * d + e] / s : 0.0f;
+      int pk = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
+      pk = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], pk, true);
+      w[d] = (uint32_t)pk;
+    }
+    *reinterpret_cast<u32x2*>(qr + 8 * (lane + 64 * i)) = u32x2{w[0], w[1]};
+  }
+  if (lane == 0) a.xs[t] = s;
+}
+
+// ---------------------------------------------------------------------------------------
+// FP8 GEMM.  Tiles of 128 tokens x 128 channels; the four waves own 64 x 64 quadrants as
+// 2 x 2 blocks of 32 x 32.  The 128-byte K stage of a 128-row operand tile is 16 KB: row r
+// holds its eight 16-byte chunks at r*128 + 16 (c ^ (r & 7)) (the swizzle keeps the
+// eight rows a read instruction's lane groups touch on distinct banks).  A direct load
+// fills one kilobyte (eight rows) per instruction: lane l writes bytes 16 l .. 16 l + 15 of
+// the block, i.e. row l / 8 and physical chunk l % 8, so it fetches logical chunk
+// (l % 8) ^ (l / 8) of that row.
+constexpr int kBM = 128, kBN = 128, kBK = 128;
+constexpr int kStageBytes = kBM * kBK;          // 16 KB per operand and stage
+constexpr int kKSteps = kHidden / kBK;          // 20
+
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"   // M0 in the clobber list: nothing else uses it
+// Direct global -> LDS load of 16 bytes per lane from a wave-uniform base plus a per-lane
+// 32-bit offset, into the 1 KB block at lds_block (lane l fills bytes 16 l .. 16 l + 15).
+// Untracked by the compiler: every wait for it is an explicit vmcnt before a barrier.
+__device__ __forceinline__ void dma16_s(const void* sbase, uint32_t voff, void* lds_block) {
+  const uint32_t lds = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)lds_block;
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :: "v"(voff), "s"(sbase), "s"(lds) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+__device__ __forceinline__ void wait_vmcnt0() {
+  __builtin_amdgcn_s_waitcnt(0 | (0x7 << 4) | (0xF << 8));   // vmcnt(0), others untouched
+}
+
+// Row r, logical 16-byte chunk c of a stage buffer.
+__device__ __forceinline__ const u32x4* stage_chunk(const uint8_t* buf, int r, int c) {
+  return reinterpret_cast<const u32x4*>(buf + r * kBK + 16 * (c ^ (r & 7)));
+}
+
+__global__ __launch_bounds__(256) void qkv_gemm_kernel(ProjArgs a) {
+  __shared__ __attribute__((aligned(1024))) uint8_t s_x[2][kStageBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t s_w[2][kStageBytes];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  constexpr int n_tiles = kQkvOut / kBN;        // 48
+  const int n_tile = blockIdx.x % n_tiles;      // consecutive workgroups share the token rows
+  const int m0 = (blockIdx.x / n_tiles) * kBM;
+  const int n0 = n_tile * kBN;
+  const int T = a.tokens;
+
+  // This wave loads blocks 4 wave .. 4 wave + 3 (rows 32 wave .. 32 wave + 31) of each
+  // operand tile; per-lane byte offsets from the operand's base (token rows past the end
+  // read the last row; their results are not stored).
+  const int lr = lane >> 3, lc = (lane & 7) ^ lr;
+  uint32_t xoff[4], woff[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = 32 * wave + 8 * i + lr;
+    xoff[i] = (uint32_t)min(m0 + r, T - 1) * kHidden + 16 * lc;
+    woff[i] = (uint32_t)(n0 + r) * kHidden + 16 * lc;
+  }
+  auto issue = [&](int stage, int k0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      dma16_s(a.xq + k0, xoff[i], &s_x[stage][(4 * wave + i) * 1024]);
+      dma16_s(a.w + k0, woff[i], &s_w[stage][(4 * wave + i) * 1024]);
+    }
+  };
+
+  const int wm = wave & 1, wn = wave >> 1;     // this wave's 64 x 64 quadrant
+  const int half = lane >> 5, r32 = lane & 31;
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
+
+  issue(0, 0);
+  wait_vmcnt0();
+  __syncthreads();
+  for (int ks = 0; ks < kKSteps; ++ks) {
+    const int st = ks & 1;
+    if (ks + 1 < kKSteps) issue(st ^ 1, (ks + 1) * kBK);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {                // two MFMA K-steps of 64 bytes per stage
+      // Lane l: row l % 32 of a 32-row block, K bytes 32 (l / 32) .. + 31 of the step:
+      // logical chunks 4 j + 2 half and + 1 (A and B take the same K order).
+      const int c0 = 4 * j + 2 * half;
+      i32x8 xf[2], wf[2];
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        const int rx = 64 * wm + 32 * b + r32, rw = 64 * wn + 32 * b + r32;
+        const u32x4 x0 = *stage_chunk(s_x[st], rx, c0), x1 = *stage_chunk(s_x[st], rx, c0 + 1);
+        const u32x4 w0 = *stage_chunk(s_w[st], rw, c0), w1 = *stage_chunk(s_w[st], rw, c0 + 1);
+        xf[b] = i32x8{(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3], (int)x1[0], (int)x1[1], (int)x1[2], (int)x1[3]};
+        wf[b] = i32x8{(int)w0[0], (int)w0[1], (int)w0[2], (int)w0[3], (int)w1[0], (int)w1[1], (int)w1[2], (int)w1[3]};
+      }
+#pragma unroll
+      for (int bm = 0; bm < 2; ++bm)
+#pragma unroll
+        for (int bn = 0; bn < 2; ++bn)
+          acc[bm][bn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(xf[bm], wf[bn], acc[bm][bn],
+                                                                        0, 0, 0, 127, 0, 127);
+    }
+    wait_vmcnt0();                               // this lane's loads of the next stage
+    __syncthreads();                             // all reads of this stage done, next visible
+  }
+
+  // Epilogue: C * s_token * s_channel -> bf16, into q, k or v (each tile lies in one).
+  uint16_t* dst;
+  int ld, col0;
+  if (n0 < kQOut) { dst = a.q; ld = kQOut; col0 = n0; }
+  else if (n0 < kQOut + kKvOut) { dst = a.k; ld = kKvOut; col0 = n0 - kQOut; }
+  else { dst = a.v; ld = kKvOut; col0 = n0 - kQOut - kKvOut; }
+#pragma unroll
+  for (int bn = 0; bn < 2; ++bn) {
+    const int c = 64 * wn + 32 * bn + r32;
+    const float sw = a.w_scale[n0 + c];
+#pragma unroll
+    for (int bm = 0; bm < 2; ++bm)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int row = m0 + 64 * wm + 32 * bm + 8 * (v >> 2) + 4 * half + (v & 3);
+        if (row < T) {
+          const float y = acc[bm][bn][v] * a.xs[row] * sw;
+          dst[(size_t)row * ld + col0 + c] = (uint16_t)(pack_bf16x2(y, 0.0f) & 0xffffu);
+        }
+      }
+  }
+}
+
+}  // namespace
+
+size_t proj_workspace_bytes(int tokens) {
+  const size_t codes = ((size_t)tokens * kHidden + 255) & ~(size_t)255;
+  return codes + (size_t)tokens * sizeof(float);
+}
+
+hipError_t launch_qkv_proj(const ProjArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL(quant_gate_kernel, dim3((a.tokens + 3) / 4), dim3(256), 0, stream, a);
+  const int m_tiles = (a.tokens + kBM - 1) / kBM;
+  hipLaunchKernelGGL(qkv_gemm_kernel, dim3(m_tiles * (kQkvOut / kBN)), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace spark

@@ -71,7 +71,24 @@ struct DecodeArgs {
   int nparts;             // P
 };
 
+// W8A8 FP8 q_k_v_proj and bf16 g_proj of T tokens.
+struct ProjArgs {
+  const uint16_t* x;        // [T, 2560] bf16 hidden states
+  const uint8_t* w;         // [6144, 2560] E4M3FN codes (rows: q 0..4095, k .., v ..)
+  const float* w_scale;     // [6144] per output channel
+  const uint16_t* w_gate;   // [16, 2560] bf16
+  uint8_t* xq;              // [T, 2560] workspace: E4M3FN codes of the activations
+  float* xs;                // [T] workspace: per-token scales
+  uint16_t* q;              // [T, 16, 256] bf16
+  uint16_t* k;              // [T, 4, 256]
+  uint16_t* v;              // [T, 4, 256]
+  uint16_t* gate;           // [T, 16]
+  int tokens;
+};
+
 hipError_t launch_prefill(int layer_type, const PrefillArgs& a, hipStream_t stream);
+hipError_t launch_qkv_proj(const ProjArgs& a, hipStream_t stream);
+size_t proj_workspace_bytes(int tokens);
 hipError_t launch_append(int layer_type, const AppendArgs& a, hipStream_t stream);
 hipError_t launch_decode(int layer_type, const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_append_q8(int layer_type, const AppendQ8Args& a, hipStream_t stream);

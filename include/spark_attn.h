@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define SPARK_ATTN_ABI_VERSION 6
+#define SPARK_ATTN_ABI_VERSION 7
 
 enum { SPARK_Q_HEADS = 16, SPARK_KV_HEADS = 4, SPARK_HEAD_DIM = 256, SPARK_WINDOW = 512 };
 
@@ -115,6 +115,35 @@ spark_status spark_attn_prefill(int32_t layer_type, int32_t batch, int32_t seq_l
                                 const void* v, const void* gate_logits,
                                 const spark_kv_cache* cache, void* workspace,
                                 size_t workspace_bytes, void* out, void* stream);
+
+/*
+ * Bytes of device workspace spark_qkv_proj_fp8 needs: the activations' FP8 codes
+ * [tokens, 2560] (padded to 256 bytes), then their per-token scales fp32 [tokens].
+ */
+size_t spark_qkv_proj_fp8_workspace_bytes(int32_t tokens);
+
+/*
+ * The projections that feed the attention, for `tokens` hidden states (Spark-X2.6-4B-FP8
+ * walkthrough, nxmr.cn/news/148448, sections 二 and 三): q_k_v_proj in W8A8 FP8 and g_proj
+ * in BF16, hidden 2560 (section 一).
+ *   x            bf16 [tokens, 2560]
+ *   w_qkv        OCP FP8 E4M3FN codes [6144, 2560]: output channels 0..4095 are q (head h
+ *                at 256h..256h+255), 4096..5119 k, 5120..6143 v
+ *   w_scale      fp32 [6144]: one scale per output channel (quantised offline)
+ *   w_gate       bf16 [16, 2560]
+ *   q, k, v      bf16 [tokens, 16, 256], [tokens, 4, 256], [tokens, 4, 256] (written):
+ *                the layouts spark_attn_prefill takes, before RoPE
+ *   gate_logits  bf16 [tokens, 16] (written)
+ *   workspace    >= spark_qkv_proj_fp8_workspace_bytes(tokens), 256-byte aligned
+ * Per token: s = max|x| / 448 and codes E4M3FN(x / s), nearest even (fp32 divisions);
+ * y = s * w_scale[n] * sum_k code_x * code_w (fp32 accumulation), rounded to bf16; gate =
+ * x w_gate^T from the bf16 values, fp32 accumulation.  1 <= tokens <= 2^20; x, w_qkv,
+ * w_gate, q, k, v 16-byte aligned.  Two launches: quantisation with the gate projection,
+ * then the FP8 GEMM on MFMA.
+ */
+spark_status spark_qkv_proj_fp8(int32_t tokens, const void* x, const void* w_qkv, const float* w_scale,
+                                const void* w_gate, void* q, void* k, void* v, void* gate_logits,
+                                void* workspace, size_t workspace_bytes, void* stream);
 
 /* Bytes of device workspace spark_attn_prefill_varlen needs: bf16 [total_tokens, 4, 256],
  * then (256-byte aligned) a 256-byte block holding the work queue of the attention launch. */

@@ -182,11 +182,13 @@ def uniform_f32(seed: int, tensor_index: int, shape, lo: float, hi: float) -> np
 
 def proj_inputs(seed: int, tokens: int) -> dict:
     """Hidden states x [T, 2560] bf16 N(0,1); q_k_v_proj weights as E4M3 codes
-    [6144, 2560] with per-channel scales in [0.003, 0.007) (outputs of order 1); g_proj
-    weights [16, 2560] bf16 N(0, 2^-12) (gate logits of order 1)."""
+    [6144, 2560] (rms of the code values about 4.9) with per-channel scales in
+    [0.0025, 0.004), so that q, k, v come out with an rms of about 0.8, like the N(0,1)
+    attention inputs elsewhere; g_proj weights [16, 2560] bf16 N(0, 2^-12) (gate logits of
+    order 1)."""
     return {
         "x": normal_bf16(seed, 0, (tokens, 2560)),
         "w": fp8_e4m3_codes(seed, 1, (6144, 2560)),
-        "w_scale": uniform_f32(seed, 2, (6144,), 0.003, 0.007),
+        "w_scale": uniform_f32(seed, 2, (6144,), 0.0025, 0.004),
         "wg": normal_bf16_scaled(seed, 3, (16, 2560), -6),
     }

@@ -30,7 +30,7 @@ def test_exports_every_declared_function():
 
 
 def test_version_and_status_strings():
-    assert fga.abi_version() == 6
+    assert fga.abi_version() == 7
     assert fga.status_string(0) == "ok"
     assert fga.status_string(3) == "workspace too small"
     assert fga.status_string(99) == "unknown status"
@@ -173,3 +173,15 @@ def test_prefill_varlen_rejects(kw, status):
 def test_prefill_varlen_workspace():
     assert fga.prefill_varlen_workspace_bytes(1, 100) == 100 * 4 * 256 * 2 + 256
     assert fga.prefill_varlen_workspace_bytes(2, 100) == 0 and fga.prefill_varlen_workspace_bytes(0, 0) == 0
+
+
+def test_qkv_proj_rejects():
+    f = lib.spark_qkv_proj_fp8
+    ok = dict(T=16, x=FAKE, w=FAKE, s=FAKE, g=FAKE, q=FAKE, k=FAKE, v=FAKE, gl=FAKE, ws=FAKE, wsb=1 << 30)
+    call = lambda **kw: f(*({**ok, **kw}[n] for n in ("T", "x", "w", "s", "g", "q", "k", "v", "gl", "ws", "wsb")), None)
+    assert call(T=0) == 1 and call(T=(1 << 20) + 1) == 1
+    assert call(x=None) == 1 and call(s=None) == 1 and call(ws=None) == 1
+    assert call(x=MISALIGNED) == 1 and call(ws=MISALIGNED) == 1 and call(s=ctypes.c_void_p(0x10002)) == 1
+    assert call(wsb=16 * 2560) == 3
+    assert fga.qkv_proj_fp8_workspace_bytes(16) == 16 * 2560 + 16 * 4
+    assert fga.qkv_proj_fp8_workspace_bytes(5) == 12800 + 20 and fga.qkv_proj_fp8_workspace_bytes(0) == 0
