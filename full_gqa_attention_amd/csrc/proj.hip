@@ -8,9 +8,9 @@
 //     16 gate logits in fp32 from the bf16 values (g_proj), s = max|x| / 448 and the OCP
 //     E4M3FN codes of x / s (v_cvt_pk_fp8_f32: nearest even), into the workspace;
 //   * qkv_gemm_kernel: C = X_q W_q^T on v_mfma_scale_f32_32x32x64_f8f6f4 (block scales 1),
-//     128 x 128 output tiles, K in stages of 128 bytes through a two-stage LDS ring filled
-//     by direct global->LDS loads; epilogue C * s_token * s_channel, rounded to bf16 and
-//     stored straight into the q, k or v layout the attention path reads.
+//     output tiles of tokens x 128 channels, K in stages of 128 bytes through an LDS ring
+//     filled by direct global->LDS loads; epilogue C * s_token * s_channel, rounded to bf16
+//     and stored straight into the q, k or v layout the attention path reads.
 #include "spark_device.hpp"
 #include "spark_launch.hpp"
 
@@ -97,15 +97,14 @@ __global__ __launch_bounds__(256) void quant_gate_kernel(ProjArgs a) {
 }
 
 // ---------------------------------------------------------------------------------------
-// FP8 GEMM.  Tiles of 128 tokens x 128 channels; the four waves own 64 x 64 quadrants as
-// 2 x 2 blocks of 32 x 32.  The 128-byte K stage of a 128-row operand tile is 16 KB: row r
-// holds its eight 16-byte chunks at r*128 + 16 (c ^ (r & 7)) (the swizzle keeps the
-// eight rows a read instruction's lane groups touch on distinct banks).  A direct load
-// fills one kilobyte (eight rows) per instruction: lane l writes bytes 16 l .. 16 l + 15 of
-// the block, i.e. row l / 8 and physical chunk l % 8, so it fetches logical chunk
-// (l % 8) ^ (l / 8) of that row.
-constexpr int kBM = 128, kBN = 128, kBK = 128;
-constexpr int kStageBytes = kBM * kBK;          // 16 KB per operand and stage
+// FP8 GEMM.  Tiles of (64 WM) tokens x 128 channels: 2 WM waves, each owning a 64 x 64
+// quadrant as 2 x 2 blocks of 32 x 32; K in stages of 128 bytes through a ring of S LDS
+// stages, each filled S - 1 stages ahead.  In a stage, operand row r holds its eight 16-byte
+// chunks at r*128 + 16 (c ^ (r & 7)) (the swizzle keeps the eight rows a read instruction's
+// lane groups touch on distinct banks).  A direct load fills one kilobyte (eight rows) per
+// instruction: lane l writes bytes 16 l .. 16 l + 15 of the block, i.e. row l / 8 and
+// physical chunk l % 8, so it fetches logical chunk (l % 8) ^ (l / 8) of that row.
+constexpr int kBK = 128;
 constexpr int kKSteps = kHidden / kBK;          // 20
 
 #pragma clang diagnostic push
@@ -123,79 +122,105 @@ __device__ __forceinline__ void dma16_s(const void* sbase, uint32_t voff, void* 
 __device__ __forceinline__ void wait_vmcnt0() {
   __builtin_amdgcn_s_waitcnt(0 | (0x7 << 4) | (0xF << 8));   // vmcnt(0), others untouched
 }
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {                // vmcnt <= N, others untouched
+  static_assert(N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
 
 // Row r, logical 16-byte chunk c of a stage buffer.
 __device__ __forceinline__ const u32x4* stage_chunk(const uint8_t* buf, int r, int c) {
   return reinterpret_cast<const u32x4*>(buf + r * kBK + 16 * (c ^ (r & 7)));
 }
 
-__global__ __launch_bounds__(256) void qkv_gemm_kernel(ProjArgs a) {
-  __shared__ __attribute__((aligned(1024))) uint8_t s_x[2][kStageBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t s_w[2][kStageBytes];
+template <int WM, int WN, int BMW, int BNW, int S>
+struct GemmShape {
+  static constexpr int kWaves = WM * WN;
+  static constexpr int kBM = 32 * BMW * WM, kBN = 32 * BNW * WN;       // workgroup tile
+  static constexpr int kXBlocks = kBM / 8, kWBlocks = kBN / 8;          // 1 KB blocks per stage
+  static constexpr int kLoads = (kXBlocks + kWBlocks) / kWaves;        // per wave and stage
+  static_assert((kXBlocks + kWBlocks) % kWaves == 0, "even load split");
+  static_assert(kQkvOut % kBN == 0 && kQOut % kBN == 0 && kKvOut % kBN == 0, "tiles inside q, k or v");
+};
+
+// Waves WM x WN; each wave owns (32 BMW) x (32 BNW) outputs as BMW x BNW blocks of 32 x 32.
+template <int WM, int WN, int BMW, int BNW, int S>
+__global__ __launch_bounds__(64 * WM * WN) void qkv_gemm_kernel(ProjArgs a) {
+  using G = GemmShape<WM, WN, BMW, BNW, S>;
+  __shared__ __attribute__((aligned(1024))) uint8_t s_x[S][G::kBM * kBK];
+  __shared__ __attribute__((aligned(1024))) uint8_t s_w[S][G::kBN * kBK];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  constexpr int n_tiles = kQkvOut / kBN;        // 48
+  constexpr int n_tiles = kQkvOut / G::kBN;
   const int n_tile = blockIdx.x % n_tiles;      // consecutive workgroups share the token rows
-  const int m0 = (blockIdx.x / n_tiles) * kBM;
-  const int n0 = n_tile * kBN;
+  const int m0 = (blockIdx.x / n_tiles) * G::kBM;
+  const int n0 = n_tile * G::kBN;
   const int T = a.tokens;
 
-  // This wave loads blocks 4 wave .. 4 wave + 3 (rows 32 wave .. 32 wave + 31) of each
-  // operand tile; per-lane byte offsets from the operand's base (token rows past the end
-  // read the last row; their results are not stored).
+  // Load i of this wave fills block (wave * kLoads + i) of the stage: first the X blocks,
+  // then the W blocks.  Per-lane byte offsets from the operand's base (token rows past the
+  // end read the last row; their results are not stored).
   const int lr = lane >> 3, lc = (lane & 7) ^ lr;
-  uint32_t xoff[4], woff[4];
+  uint32_t off[G::kLoads];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = 32 * wave + 8 * i + lr;
-    xoff[i] = (uint32_t)min(m0 + r, T - 1) * kHidden + 16 * lc;
-    woff[i] = (uint32_t)(n0 + r) * kHidden + 16 * lc;
+  for (int i = 0; i < G::kLoads; ++i) {
+    const int blk = wave * G::kLoads + i;
+    off[i] = blk < G::kXBlocks ? (uint32_t)min(m0 + 8 * blk + lr, T - 1) * kHidden + 16 * lc
+                               : (uint32_t)(n0 + 8 * (blk - G::kXBlocks) + lr) * kHidden + 16 * lc;
   }
   auto issue = [&](int stage, int k0) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      dma16_s(a.xq + k0, xoff[i], &s_x[stage][(4 * wave + i) * 1024]);
-      dma16_s(a.w + k0, woff[i], &s_w[stage][(4 * wave + i) * 1024]);
+    for (int i = 0; i < G::kLoads; ++i) {
+      const int blk = wave * G::kLoads + i;
+      if (blk < G::kXBlocks) dma16_s(a.xq + k0, off[i], &s_x[stage][blk * 1024]);
+      else dma16_s(a.w + k0, off[i], &s_w[stage][(blk - G::kXBlocks) * 1024]);
     }
   };
 
-  const int wm = wave & 1, wn = wave >> 1;     // this wave's 64 x 64 quadrant
+  const int wm = wave % WM, wn = wave / WM;     // this wave's tile
   const int half = lane >> 5, r32 = lane & 31;
-  f32x16 acc[2][2];
+  f32x16 acc[BMW][BNW];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < BMW; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
+    for (int j = 0; j < BNW; ++j) acc[i][j] = f32x16{};
 
-  issue(0, 0);
-  wait_vmcnt0();
+#pragma unroll
+  for (int p = 0; p < S - 1; ++p) issue(p, p * kBK);
+  if constexpr (S == 2) wait_vmcnt0(); else wait_vmcnt<G::kLoads * (S - 2)>();
   __syncthreads();
   for (int ks = 0; ks < kKSteps; ++ks) {
-    const int st = ks & 1;
-    if (ks + 1 < kKSteps) issue(st ^ 1, (ks + 1) * kBK);
+    const int st = ks % S;
+    const bool ahead = ks + S - 1 < kKSteps;
+    if (ahead) issue((ks + S - 1) % S, (ks + S - 1) * kBK);
 #pragma unroll
     for (int j = 0; j < 2; ++j) {                // two MFMA K-steps of 64 bytes per stage
       // Lane l: row l % 32 of a 32-row block, K bytes 32 (l / 32) .. + 31 of the step:
       // logical chunks 4 j + 2 half and + 1 (A and B take the same K order).
       const int c0 = 4 * j + 2 * half;
-      i32x8 xf[2], wf[2];
+      i32x8 xf[BMW], wf[BNW];
 #pragma unroll
-      for (int b = 0; b < 2; ++b) {
-        const int rx = 64 * wm + 32 * b + r32, rw = 64 * wn + 32 * b + r32;
+      for (int b = 0; b < BMW; ++b) {
+        const int rx = 32 * (BMW * wm + b) + r32;
         const u32x4 x0 = *stage_chunk(s_x[st], rx, c0), x1 = *stage_chunk(s_x[st], rx, c0 + 1);
-        const u32x4 w0 = *stage_chunk(s_w[st], rw, c0), w1 = *stage_chunk(s_w[st], rw, c0 + 1);
         xf[b] = i32x8{(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3], (int)x1[0], (int)x1[1], (int)x1[2], (int)x1[3]};
+      }
+#pragma unroll
+      for (int b = 0; b < BNW; ++b) {
+        const int rw = 32 * (BNW * wn + b) + r32;
+        const u32x4 w0 = *stage_chunk(s_w[st], rw, c0), w1 = *stage_chunk(s_w[st], rw, c0 + 1);
         wf[b] = i32x8{(int)w0[0], (int)w0[1], (int)w0[2], (int)w0[3], (int)w1[0], (int)w1[1], (int)w1[2], (int)w1[3]};
       }
 #pragma unroll
-      for (int bm = 0; bm < 2; ++bm)
+      for (int bm = 0; bm < BMW; ++bm)
 #pragma unroll
-        for (int bn = 0; bn < 2; ++bn)
+        for (int bn = 0; bn < BNW; ++bn)
           acc[bm][bn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(xf[bm], wf[bn], acc[bm][bn],
                                                                         0, 0, 0, 127, 0, 127);
     }
-    wait_vmcnt0();                               // this lane's loads of the next stage
-    __syncthreads();                             // all reads of this stage done, next visible
+    // Stage ks + 1 must have landed; the S - 2 stages issued after it may still be in flight.
+    if (S > 2 && ahead) wait_vmcnt<G::kLoads * (S - 2)>(); else wait_vmcnt0();
+    __syncthreads();                             // reads of this stage done, next visible
   }
 
   // Epilogue: C * s_token * s_channel -> bf16, into q, k or v (each tile lies in one).
@@ -205,14 +230,14 @@ __global__ __launch_bounds__(256) void qkv_gemm_kernel(ProjArgs a) {
   else if (n0 < kQOut + kKvOut) { dst = a.k; ld = kKvOut; col0 = n0 - kQOut; }
   else { dst = a.v; ld = kKvOut; col0 = n0 - kQOut - kKvOut; }
 #pragma unroll
-  for (int bn = 0; bn < 2; ++bn) {
-    const int c = 64 * wn + 32 * bn + r32;
+  for (int bn = 0; bn < BNW; ++bn) {
+    const int c = 32 * (BNW * wn + bn) + r32;
     const float sw = a.w_scale[n0 + c];
 #pragma unroll
-    for (int bm = 0; bm < 2; ++bm)
+    for (int bm = 0; bm < BMW; ++bm)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int row = m0 + 64 * wm + 32 * bm + 8 * (v >> 2) + 4 * half + (v & 3);
+        const int row = m0 + 32 * (BMW * wm + bm) + 8 * (v >> 2) + 4 * half + (v & 3);
         if (row < T) {
           const float y = acc[bm][bn][v] * a.xs[row] * sw;
           dst[(size_t)row * ld + col0 + c] = (uint16_t)(pack_bf16x2(y, 0.0f) & 0xffffu);
@@ -220,6 +245,12 @@ __global__ __launch_bounds__(256) void qkv_gemm_kernel(ProjArgs a) {
       }
   }
 }
+
+#ifndef SPARK_GEMM_CFG
+#define SPARK_GEMM_CFG 4, 2, 2, 2, 3
+#endif
+#define SPARK_GEMM_KERNEL qkv_gemm_kernel<SPARK_GEMM_CFG>
+using GemmCfg = GemmShape<SPARK_GEMM_CFG>;
 
 }  // namespace
 
@@ -230,8 +261,9 @@ size_t proj_workspace_bytes(int tokens) {
 
 hipError_t launch_qkv_proj(const ProjArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL(quant_gate_kernel, dim3((a.tokens + 3) / 4), dim3(256), 0, stream, a);
-  const int m_tiles = (a.tokens + kBM - 1) / kBM;
-  hipLaunchKernelGGL(qkv_gemm_kernel, dim3(m_tiles * (kQkvOut / kBN)), dim3(256), 0, stream, a);
+  const int m_tiles = (a.tokens + GemmCfg::kBM - 1) / GemmCfg::kBM;
+  hipLaunchKernelGGL((SPARK_GEMM_KERNEL), dim3(m_tiles * (kQkvOut / GemmCfg::kBN)),
+                     dim3(64 * GemmCfg::kWaves), 0, stream, a);
   return hipGetLastError();
 }
 
