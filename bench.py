@@ -26,6 +26,7 @@ sys.path.insert(0, ROOT)
 METRIC = "attention tokens/s (prefill, % MFMA peak) + decode KV GB/s (% HBM peak)"
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+PEAK_FP8_TFLOPS = 5000.0       # MI355X dense fp8 MFMA
 
 
 def log(msg):
@@ -342,6 +343,29 @@ def bench_configs(fga, synth):
         log(f"36-layer decode step, batch 64 ({kv} cache): {ms:.2f} ms  {B / (ms * 1e-3):.0f} tokens/s  "
             f"{nbytes / (ms * 1e-3) / 1e9:.0f} GB/s")
         del layers
+        torch.cuda.empty_cache()
+    # The W8A8 FP8 q/k/v projection with the bf16 gate projection upstream of the path:
+    # T tokens of hidden 2560 -> 6144 q/k/v channels (+ 16 gate logits).
+    for T in (8192, 32768):
+        gen.manual_seed(synth.CONFIG_SEED[1] + 400 + T)
+        x = dev_normal(gen, (T, 2560))
+        w = torch.randint(0x18, 0x50, (6144, 2560), generator=gen, device="cuda", dtype=torch.uint8)
+        w = torch.where(torch.rand(w.shape, generator=gen, device="cuda") < 0.5, w, w | 0x80)
+        wsc = 0.0025 + 0.0015 * torch.rand(6144, generator=gen, device="cuda")
+        wg = (dev_normal(gen, (16, 2560)).float() / 64).to(torch.bfloat16)
+        outs = (torch.empty(T, 16, 256, dtype=torch.bfloat16, device="cuda"),
+                torch.empty(T, 4, 256, dtype=torch.bfloat16, device="cuda"),
+                torch.empty(T, 4, 256, dtype=torch.bfloat16, device="cuda"),
+                torch.empty(T, 16, dtype=torch.bfloat16, device="cuda"))
+        wsp = torch.empty(fga.qkv_proj_fp8_workspace_bytes(T), dtype=torch.uint8, device="cuda")
+        ms = time_launches(lambda: fga.qkv_proj_fp8(x, w, wsc, wg, out=outs, workspace=wsp), 20, 5)
+        flops = 2 * T * 2560 * 6144
+        out[f"qkv_proj_fp8_t{T}"] = {"us": ms * 1e3, "tflops_fp8": flops / (ms * 1e-3) / 1e12,
+                                     "frac_fp8_mfma": flops / (ms * 1e-3) / 1e12 / PEAK_FP8_TFLOPS,
+                                     "gate_gflops_bf16": 2 * T * 2560 * 16 / 1e9}
+        log(f"FP8 q/k/v + bf16 gate projection T={T}: {ms * 1e3:.0f} us  "
+            f"{flops / (ms * 1e-3) / 1e12:.0f} TFLOP/s (fp8 GEMM flops)")
+        del x, w, wsc, wg, outs, wsp
         torch.cuda.empty_cache()
     return out
 

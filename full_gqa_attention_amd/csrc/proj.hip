@@ -4,9 +4,10 @@
 // dynamic scale; g_proj in BF16.  Hidden 2560 -> q 4096, k 1024, v 1024 (section 一).
 //
 // Two launches:
-//   * quant_gate_kernel: one wave per token reads its 2560 hidden values once, computes the
-//     16 gate logits in fp32 from the bf16 values (g_proj), s = max|x| / 448 and the OCP
-//     E4M3FN codes of x / s (v_cvt_pk_fp8_f32: nearest even), into the workspace;
+//   * quant_gate_kernel: 16 tokens per workgroup read their hidden values once, compute the
+//     16 gate logits from the bf16 values on v_mfma_f32_16x16x32_bf16 (fp32 accumulation,
+//     g_proj), s = max|x| / 448 and the OCP E4M3FN codes of x / s (v_cvt_pk_fp8_f32:
+//     nearest even), into the workspace;
 //   * qkv_gemm_kernel: C = X_q W_q^T on v_mfma_scale_f32_32x32x64_f8f6f4 (block scales 1),
 //     output tiles of tokens x 128 channels, K in stages of 128 bytes through an LDS ring
 //     filled by direct global->LDS loads; epilogue C * s_token * s_channel, rounded to bf16
@@ -27,73 +28,70 @@ constexpr float kE4M3Max = 448.0f;
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 // ---------------------------------------------------------------------------------------
-// Quantisation of the activations and the bf16 gate projection, one wave per token.
-// Lane l holds the 16-byte chunks l + 64 i (i < 5) of the row: each load is one
-// contiguous kilobyte across the wave.
+// Quantisation of the activations and the bf16 gate projection.  A workgroup of 4 waves
+// takes 16 tokens; wave w holds the hidden slice [640 w, 640 w + 640) of all 16 in
+// registers.  In K step s (32 values) lane l holds the 8 values of token l % 16 at
+// 640 w + 32 s + 8 (l / 16): the A operand of v_mfma_f32_16x16x32_bf16, whose B operand is
+// the same slice of gate row l % 16 (so the gate weights are read once per 16 tokens).
+// The 4 waves' 16 x 16 partial logits and per-token maxima meet in LDS.
+constexpr int kQgTokens = 16, kQgWaves = 4;
+constexpr int kQgSlice = kHidden / kQgWaves;   // 640
+constexpr int kQgSteps = kQgSlice / 32;        // 20
+
 __global__ __launch_bounds__(256) void quant_gate_kernel(ProjArgs a) {
-  const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= a.tokens) return;                                   // whole wave
-  const uint16_t* xr = a.x + (size_t)t * kHidden;
-  float xv[40];
+  __shared__ float s_gate[kQgWaves][kQgTokens * kGates];
+  __shared__ float s_max[kQgWaves][kQgTokens];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int t0 = blockIdx.x * kQgTokens;
+  const int tr = lane & 15;
+  const int t = min(t0 + tr, a.tokens - 1);    // rows past the end re-read the last row
+  const int k0 = wave * kQgSlice + 8 * (lane >> 4);
+  const uint16_t* xr = a.x + (size_t)t * kHidden + k0;
+  const uint16_t* gr = a.w_gate + (size_t)tr * kHidden + k0;
+  u32x4 xv[kQgSteps];
 #pragma unroll
-  for (int i = 0; i < 5; ++i) {
-    const u32x4 r = ld_global16(xr + 8 * (lane + 64 * i));
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      xv[8 * i + 2 * w] = bf16_lo(r[w]);
-      xv[8 * i + 2 * w + 1] = bf16_hi(r[w]);
-    }
-  }
-  // g_proj in bf16: 16 dot products, fp32 partial sums per lane, then across the wave.
-  float gl[kGates];
-#pragma unroll
-  for (int h = 0; h < kGates; ++h) {
-    float acc = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 5; ++i) {
-      const u32x4 r = ld_global16(a.w_gate + (size_t)h * kHidden + 8 * (lane + 64 * i));
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        acc = fmaf(xv[8 * i + 2 * w], bf16_lo(r[w]), acc);
-        acc = fmaf(xv[8 * i + 2 * w + 1], bf16_hi(r[w]), acc);
-      }
-    }
-    gl[h] = acc;
-  }
-#pragma unroll
-  for (int h = 0; h < kGates; ++h)
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) gl[h] += __shfl_xor(gl[h], off);
-  if (lane < kGates) {
-    float g = gl[0];
-#pragma unroll
-    for (int h = 1; h < kGates; ++h) g = lane == h ? gl[h] : g;
-    a.gate[(size_t)t * kGates + lane] = (uint16_t)(pack_bf16x2(g, 0.0f) & 0xffffu);
-  }
-  // Per-token FP8: s = max|x| / 448, codes E4M3FN(x / s), both divisions IEEE fp32.
+  for (int s = 0; s < kQgSteps; ++s) xv[s] = ld_global16(xr + 32 * s);
+  f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
   float m = 0.0f;
 #pragma unroll
-  for (int j = 0; j < 40; ++j) m = fmaxf(m, fabsf(xv[j]));
+  for (int s = 0; s < kQgSteps; ++s) {
+    const u32x4 g = ld_global16(gr + 32 * s);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xv[s]), as_bf16x8(g), acc, 0, 0, 0);
 #pragma unroll
-  for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
-  const float s = m / kE4M3Max;
-  uint8_t* qr = a.xq + (size_t)t * kHidden;
+    for (int w = 0; w < 4; ++w) m = fmaxf(m, fmaxf(fabsf(bf16_lo(xv[s][w])), fabsf(bf16_hi(xv[s][w]))));
+  }
+  m = fmaxf(m, __shfl_xor(m, 16));
+  m = fmaxf(m, __shfl_xor(m, 32));
+  if (lane < kQgTokens) s_max[wave][lane] = m;
+  // Output element v of lane l is logit (token 4 (l / 16) + v, gate l % 16).
 #pragma unroll
-  for (int i = 0; i < 5; ++i) {
+  for (int v = 0; v < 4; ++v) s_gate[wave][(4 * (lane >> 4) + v) * kGates + tr] = acc[v];
+  __syncthreads();
+  {
+    const int i = threadIdx.x;                   // (token i / 16, gate i % 16)
+    const float g = s_gate[0][i] + s_gate[1][i] + s_gate[2][i] + s_gate[3][i];
+    if (t0 + i / kGates < a.tokens) a.gate[(size_t)t0 * kGates + i] = (uint16_t)(pack_bf16x2(g, 0.0f) & 0xffffu);
+  }
+  // Per-token FP8: s = max|x| / 448, codes E4M3FN(x / s), both divisions IEEE fp32.
+  const float mt = fmaxf(fmaxf(s_max[0][tr], s_max[1][tr]), fmaxf(s_max[2][tr], s_max[3][tr]));
+  const float sc = mt / kE4M3Max;
+  if (t0 + tr >= a.tokens) return;
+  uint8_t* qr = a.xq + (size_t)t * kHidden + k0;
+#pragma unroll
+  for (int s = 0; s < kQgSteps; ++s) {
     uint32_t w[2];
 #pragma unroll
     for (int d = 0; d < 2; ++d) {
-      float y[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) y[e] = s > 0.0f ? xv[8 * i + 4 * d + e] / s : 0.0f;
-      int pk = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
-      pk = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], pk, true);
+      const uint32_t p0 = xv[s][2 * d], p1 = xv[s][2 * d + 1];
+      const float y0 = sc > 0.0f ? bf16_lo(p0) / sc : 0.0f, y1 = sc > 0.0f ? bf16_hi(p0) / sc : 0.0f;
+      const float y2 = sc > 0.0f ? bf16_lo(p1) / sc : 0.0f, y3 = sc > 0.0f ? bf16_hi(p1) / sc : 0.0f;
+      int pk = __builtin_amdgcn_cvt_pk_fp8_f32(y0, y1, 0, false);
+      pk = __builtin_amdgcn_cvt_pk_fp8_f32(y2, y3, pk, true);
       w[d] = (uint32_t)pk;
     }
-    *reinterpret_cast<u32x2*>(qr + 8 * (lane + 64 * i)) = u32x2{w[0], w[1]};
+    *reinterpret_cast<u32x2*>(qr + 32 * s) = u32x2{w[0], w[1]};
   }
-  if (lane == 0) a.xs[t] = s;
+  if (wave == 0 && lane < kQgTokens) a.xs[t] = sc;
 }
 
 // ---------------------------------------------------------------------------------------
@@ -260,7 +258,7 @@ size_t proj_workspace_bytes(int tokens) {
 }
 
 hipError_t launch_qkv_proj(const ProjArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL(quant_gate_kernel, dim3((a.tokens + 3) / 4), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(quant_gate_kernel, dim3((a.tokens + kQgTokens - 1) / kQgTokens), dim3(256), 0, stream, a);
   const int m_tiles = (a.tokens + GemmCfg::kBM - 1) / GemmCfg::kBM;
   hipLaunchKernelGGL((SPARK_GEMM_KERNEL), dim3(m_tiles * (kQkvOut / GemmCfg::kBN)),
                      dim3(64 * GemmCfg::kWaves), 0, stream, a);
