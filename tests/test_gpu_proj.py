@@ -27,7 +27,7 @@ def _assert_close(got, want, what, sum_abs):
     """bf16 outputs of long sums: within one bf16 rounding of the exact value (2^-9
     relative, taken as 2^-8) plus 2^-16 of the sum of the terms' magnitudes -- the dot
     product bound; the FP8 MFMA adds the 64 products of a step at less than fp32 precision
-    (about 2^-18 of that sum was seen), the fp32 FMAs of the gate far less.  Relative L2 <= 5e-3."""
+    (about 2^-18 of that sum was seen), the gate's bf16 MFMA (fp32 sums) far less.  Relative L2 <= 5e-3."""
     got = np.asarray(got, np.float64)
     want = np.asarray(want, np.float64)
     assert np.all(np.isfinite(got)), f"{what}: non-finite output"
