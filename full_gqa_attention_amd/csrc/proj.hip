@@ -95,15 +95,14 @@ __global__ __launch_bounds__(256) void quant_gate_kernel(ProjArgs a) {
 }
 
 // ---------------------------------------------------------------------------------------
-// FP8 GEMM.  Tiles of (64 WM) tokens x 128 channels: 2 WM waves, each owning a 64 x 64
-// quadrant as 2 x 2 blocks of 32 x 32; K in stages of 128 bytes through a ring of S LDS
-// stages, each filled S - 1 stages ahead.  In a stage, operand row r holds its eight 16-byte
-// chunks at r*128 + 16 (c ^ (r & 7)) (the swizzle keeps the eight rows a read instruction's
-// lane groups touch on distinct banks).  A direct load fills one kilobyte (eight rows) per
-// instruction: lane l writes bytes 16 l .. 16 l + 15 of the block, i.e. row l / 8 and
-// physical chunk l % 8, so it fetches logical chunk (l % 8) ^ (l / 8) of that row.
-constexpr int kBK = 128;
-constexpr int kKSteps = kHidden / kBK;          // 20
+// FP8 GEMM.  Workgroup tiles of tokens x channels on WM x WN waves, each wave owning
+// BMW x BNW blocks of 32 x 32; K in stages of BK bytes (64 or 128) through a ring of S LDS
+// stages, each filled S - 1 stages ahead.  In a stage, operand row r holds its BK / 16
+// chunks of 16 bytes at r BK + 16 (c ^ swz(r)) with swz(r) = r & 7 (BK = 128) or
+// (r / 4) & 3 (BK = 64): the rows one read instruction's lane groups touch then hit
+// distinct banks.  A direct load fills one kilobyte (1024 / BK rows) per instruction: lane
+// l writes bytes 16 l .. 16 l + 15 of the block, i.e. row l / (BK / 16) and physical chunk
+// l % (BK / 16), so it fetches the logical chunk whose swizzled place that is.
 
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"   // M0 in the clobber list: nothing else uses it
@@ -126,27 +125,36 @@ __device__ __forceinline__ void wait_vmcnt() {                // vmcnt <= N, oth
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
+template <int BK>
+__device__ __forceinline__ int swz(int r) { return BK == 128 ? (r & 7) : ((r >> 2) & 3); }
+
 // Row r, logical 16-byte chunk c of a stage buffer.
+template <int BK>
 __device__ __forceinline__ const u32x4* stage_chunk(const uint8_t* buf, int r, int c) {
-  return reinterpret_cast<const u32x4*>(buf + r * kBK + 16 * (c ^ (r & 7)));
+  return reinterpret_cast<const u32x4*>(buf + r * BK + 16 * (c ^ swz<BK>(r)));
 }
 
-template <int WM, int WN, int BMW, int BNW, int S>
+template <int WM, int WN, int BMW, int BNW, int S, int BK>
 struct GemmShape {
+  static_assert(BK == 64 || BK == 128, "stage depth");
   static constexpr int kWaves = WM * WN;
   static constexpr int kBM = 32 * BMW * WM, kBN = 32 * BNW * WN;       // workgroup tile
-  static constexpr int kXBlocks = kBM / 8, kWBlocks = kBN / 8;          // 1 KB blocks per stage
+  static constexpr int kChunks = BK / 16, kBlockRows = 1024 / BK;
+  static constexpr int kKSteps = kHidden / BK;                          // stages over K
+  static constexpr int kXBlocks = kBM / kBlockRows, kWBlocks = kBN / kBlockRows;  // 1 KB blocks
   static constexpr int kLoads = (kXBlocks + kWBlocks) / kWaves;        // per wave and stage
-  static_assert((kXBlocks + kWBlocks) % kWaves == 0, "even load split");
+  static constexpr int kXLoads = kXBlocks / kWaves;                    // loads i < kXLoads are X
+  static_assert(kXBlocks % kWaves == 0 && kWBlocks % kWaves == 0, "even load split");
   static_assert(kQkvOut % kBN == 0 && kQOut % kBN == 0 && kKvOut % kBN == 0, "tiles inside q, k or v");
 };
 
 // Waves WM x WN; each wave owns (32 BMW) x (32 BNW) outputs as BMW x BNW blocks of 32 x 32.
-template <int WM, int WN, int BMW, int BNW, int S>
+template <int WM, int WN, int BMW, int BNW, int S, int BK>
 __global__ __launch_bounds__(64 * WM * WN) void qkv_gemm_kernel(ProjArgs a) {
-  using G = GemmShape<WM, WN, BMW, BNW, S>;
-  __shared__ __attribute__((aligned(1024))) uint8_t s_x[S][G::kBM * kBK];
-  __shared__ __attribute__((aligned(1024))) uint8_t s_w[S][G::kBN * kBK];
+  using G = GemmShape<WM, WN, BMW, BNW, S, BK>;
+  constexpr int kKSteps = G::kKSteps;
+  __shared__ __attribute__((aligned(1024))) uint8_t s_x[S][G::kBM * BK];
+  __shared__ __attribute__((aligned(1024))) uint8_t s_w[S][G::kBN * BK];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   constexpr int n_tiles = kQkvOut / G::kBN;
@@ -155,23 +163,24 @@ __global__ __launch_bounds__(64 * WM * WN) void qkv_gemm_kernel(ProjArgs a) {
   const int n0 = n_tile * G::kBN;
   const int T = a.tokens;
 
-  // Load i of this wave fills block (wave * kLoads + i) of the stage: first the X blocks,
-  // then the W blocks.  Per-lane byte offsets from the operand's base (token rows past the
-  // end read the last row; their results are not stored).
-  const int lr = lane >> 3, lc = (lane & 7) ^ lr;
+  // Load i of this wave fills X block wave + kWaves i (i < kXLoads), else W block
+  // wave + kWaves (i - kXLoads): which operand is known at compile time.  Per-lane byte
+  // offsets from the operand's base (token rows past the end read the last row; their
+  // results are not stored).
+  const int lr = lane / G::kChunks, lc = (lane % G::kChunks) ^ swz<BK>(lr);
   uint32_t off[G::kLoads];
 #pragma unroll
   for (int i = 0; i < G::kLoads; ++i) {
-    const int blk = wave * G::kLoads + i;
-    off[i] = blk < G::kXBlocks ? (uint32_t)min(m0 + 8 * blk + lr, T - 1) * kHidden + 16 * lc
-                               : (uint32_t)(n0 + 8 * (blk - G::kXBlocks) + lr) * kHidden + 16 * lc;
+    const int blk = wave + G::kWaves * (i < G::kXLoads ? i : i - G::kXLoads);
+    off[i] = i < G::kXLoads ? (uint32_t)min(m0 + G::kBlockRows * blk + lr, T - 1) * kHidden + 16 * lc
+                            : (uint32_t)(n0 + G::kBlockRows * blk + lr) * kHidden + 16 * lc;
   }
   auto issue = [&](int stage, int k0) {
 #pragma unroll
     for (int i = 0; i < G::kLoads; ++i) {
-      const int blk = wave * G::kLoads + i;
-      if (blk < G::kXBlocks) dma16_s(a.xq + k0, off[i], &s_x[stage][blk * 1024]);
-      else dma16_s(a.w + k0, off[i], &s_w[stage][(blk - G::kXBlocks) * 1024]);
+      const int blk = wave + G::kWaves * (i < G::kXLoads ? i : i - G::kXLoads);
+      if (i < G::kXLoads) dma16_s(a.xq + k0, off[i], &s_x[stage][blk * 1024]);
+      else dma16_s(a.w + k0, off[i], &s_w[stage][blk * 1024]);
     }
   };
 
@@ -184,15 +193,12 @@ __global__ __launch_bounds__(64 * WM * WN) void qkv_gemm_kernel(ProjArgs a) {
     for (int j = 0; j < BNW; ++j) acc[i][j] = f32x16{};
 
 #pragma unroll
-  for (int p = 0; p < S - 1; ++p) issue(p, p * kBK);
+  for (int p = 0; p < S - 1; ++p) issue(p, p * BK);
   if constexpr (S == 2) wait_vmcnt0(); else wait_vmcnt<G::kLoads * (S - 2)>();
   __syncthreads();
-  for (int ks = 0; ks < kKSteps; ++ks) {
-    const int st = ks % S;
-    const bool ahead = ks + S - 1 < kKSteps;
-    if (ahead) issue((ks + S - 1) % S, (ks + S - 1) * kBK);
+  auto compute = [&](int st) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {                // two MFMA K-steps of 64 bytes per stage
+    for (int j = 0; j < BK / 64; ++j) {          // MFMA K-steps of 64 bytes per stage
       // Lane l: row l % 32 of a 32-row block, K bytes 32 (l / 32) .. + 31 of the step:
       // logical chunks 4 j + 2 half and + 1 (A and B take the same K order).
       const int c0 = 4 * j + 2 * half;
@@ -200,13 +206,13 @@ __global__ __launch_bounds__(64 * WM * WN) void qkv_gemm_kernel(ProjArgs a) {
 #pragma unroll
       for (int b = 0; b < BMW; ++b) {
         const int rx = 32 * (BMW * wm + b) + r32;
-        const u32x4 x0 = *stage_chunk(s_x[st], rx, c0), x1 = *stage_chunk(s_x[st], rx, c0 + 1);
+        const u32x4 x0 = *stage_chunk<BK>(s_x[st], rx, c0), x1 = *stage_chunk<BK>(s_x[st], rx, c0 + 1);
         xf[b] = i32x8{(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3], (int)x1[0], (int)x1[1], (int)x1[2], (int)x1[3]};
       }
 #pragma unroll
       for (int b = 0; b < BNW; ++b) {
         const int rw = 32 * (BNW * wn + b) + r32;
-        const u32x4 w0 = *stage_chunk(s_w[st], rw, c0), w1 = *stage_chunk(s_w[st], rw, c0 + 1);
+        const u32x4 w0 = *stage_chunk<BK>(s_w[st], rw, c0), w1 = *stage_chunk<BK>(s_w[st], rw, c0 + 1);
         wf[b] = i32x8{(int)w0[0], (int)w0[1], (int)w0[2], (int)w0[3], (int)w1[0], (int)w1[1], (int)w1[2], (int)w1[3]};
       }
 #pragma unroll
@@ -216,9 +222,26 @@ __global__ __launch_bounds__(64 * WM * WN) void qkv_gemm_kernel(ProjArgs a) {
           acc[bm][bn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(xf[bm], wf[bn], acc[bm][bn],
                                                                         0, 0, 0, 127, 0, 127);
     }
-    // Stage ks + 1 must have landed; the S - 2 stages issued after it may still be in flight.
-    if (S > 2 && ahead) wait_vmcnt<G::kLoads * (S - 2)>(); else wait_vmcnt0();
+  };
+  // Main loop: stage ks + S - 1 is issued, stage ks computed; then stage ks + 1 must have
+  // landed while the S - 2 stages issued after it may still be in flight.  The wait sits in
+  // the same basic block as the MFMAs and behind a scheduling barrier, so that the MFMAs
+  // are issued first (hoisted above them, the wait stalls on the next stage before this
+  // one is computed).
+  int ks = 0;
+  for (; ks + S - 1 < kKSteps; ++ks) {
+    issue((ks + S - 1) % S, (ks + S - 1) * BK);
+    compute(ks % S);
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (S > 2) wait_vmcnt<G::kLoads * (S - 2)>(); else wait_vmcnt0();
     __syncthreads();                             // reads of this stage done, next visible
+  }
+  // The last S - 1 stages are already issued.
+  for (; ks < kKSteps; ++ks) {
+    compute(ks % S);
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vmcnt0();
+    __syncthreads();
   }
 
   // Epilogue: C * s_token * s_channel -> bf16, into q, k or v (each tile lies in one).
@@ -245,7 +268,7 @@ __global__ __launch_bounds__(64 * WM * WN) void qkv_gemm_kernel(ProjArgs a) {
 }
 
 #ifndef SPARK_GEMM_CFG
-#define SPARK_GEMM_CFG 4, 2, 2, 2, 3
+#define SPARK_GEMM_CFG 4, 2, 2, 4, 2, 128
 #endif
 #define SPARK_GEMM_KERNEL qkv_gemm_kernel<SPARK_GEMM_CFG>
 using GemmCfg = GemmShape<SPARK_GEMM_CFG>;
