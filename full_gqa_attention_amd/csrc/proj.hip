@@ -9,8 +9,8 @@
 //     g_proj), s = max|x| / 448 and the OCP E4M3FN codes of x / s (v_cvt_pk_fp8_f32:
 //     nearest even), into the workspace;
 //   * qkv_gemm_kernel: C = X_q W_q^T on v_mfma_scale_f32_32x32x64_f8f6f4 (block scales 1),
-//     output tiles of tokens x 128 channels, K in stages of 128 bytes through an LDS ring
-//     filled by direct global->LDS loads; epilogue C * s_token * s_channel, rounded to bf16
+//     output tiles of 256 tokens x 256 channels on 8 waves, K in stages of 128 bytes
+//     through an LDS ring filled by direct global->LDS loads; epilogue C * s_token * s_channel, rounded to bf16
 //     and stored straight into the q, k or v layout the attention path reads.
 #include "spark_device.hpp"
 #include "spark_launch.hpp"
