@@ -58,7 +58,7 @@ def time_launches(fn, steps, warmup):
 
 def bench_prefill(fga, synth, steps, warmup, S=8192):
     import torch
-    inp = synth.prefill_inputs(synth.CONFIG_SEED[2], 1, S)
+    inp = synth.prefill_inputs(synth.SEED_FULL_S8192, 1, S)
     q, k, v, g = (to_dev(inp[n]) for n in ("q", "k", "v", "gate"))
     out = torch.empty_like(q)
     ws = torch.empty(fga.prefill_workspace_bytes(fga.FULL, 1, S), dtype=torch.uint8, device="cuda")
@@ -77,7 +77,7 @@ def bench_prefill(fga, synth, steps, warmup, S=8192):
 def bench_decode(fga, synth, steps, warmup):
     import numpy as np
     import torch
-    seed = synth.CONFIG_SEED[3]
+    seed = synth.SEED_DECODE_B64
     B, cap = 64, 32768
     lens = synth.decode_seq_lens(seed, B, 1024, 32768)
     q = to_dev(synth.normal_bf16(seed, 0, (B, 16, 256)))
@@ -141,9 +141,9 @@ def bench_configs(fga, synth):
     out = {}
     gen = torch.Generator(device="cuda")
 
-    # Config 1: one sliding layer, batch 1, S = 1024 (host-drawn inputs, as in the tests).
+    # One sliding layer, batch 1, S = 1024 (host-drawn inputs, as in the tests).
     S = 1024
-    inp = synth.prefill_inputs(synth.CONFIG_SEED[1], 1, S)
+    inp = synth.prefill_inputs(synth.SEED_SLIDING_S1024, 1, S)
     q, k, v, g = (to_dev(inp[n]) for n in ("q", "k", "v", "gate"))
     o = torch.empty_like(q)
     ws = torch.empty(fga.prefill_workspace_bytes(fga.SLIDING, 1, S), dtype=torch.uint8, device="cuda")
@@ -151,13 +151,13 @@ def bench_configs(fga, synth):
     tf = 16384 * sliding_pairs(S) / (ms * 1e-3) / 1e12
     out["sliding_prefill_s1024"] = {"ms": ms, "tflops": tf, "frac_mfma": tf / PEAK_BF16_TFLOPS,
                                     "tokens_per_s": S / (ms * 1e-3)}
-    log(f"config 1 sliding prefill S=1024: {ms * 1e3:.1f} us  {tf:.0f} TFLOP/s")
+    log(f"sliding prefill S=1024: {ms * 1e3:.1f} us  {tf:.0f} TFLOP/s")
     del q, k, v, g, o, ws
 
     # Chunked prefill: a chunk of 8192 tokens after a cached prefix of 8192, batch 1, each
     # layer type (the prefix's keys are read from the cache, device-drawn N(0,1)).
     P = n = 8192
-    gen.manual_seed(synth.CONFIG_SEED[2] + 100)
+    gen.manual_seed(synth.SEED_FULL_S8192 + 100)
     q, k, v, g = (dev_normal(gen, (1, n, 16, 256)), dev_normal(gen, (1, n, 4, 256)),
                   dev_normal(gen, (1, n, 4, 256)), dev_normal(gen, (1, n, 16)))
     o = torch.empty_like(q)
@@ -176,10 +176,10 @@ def bench_configs(fga, synth):
     del q, k, v, g, o
 
     # Variable-length batch: 16 sequences of lengths uniform in [512, 8192], packed.
-    lens = np.random.default_rng(synth.CONFIG_SEED[2] + 200).integers(512, 8193, size=16)
+    lens = np.random.default_rng(synth.SEED_FULL_S8192 + 200).integers(512, 8193, size=16)
     T = int(lens.sum())
     cu = torch.as_tensor(np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)).cuda()
-    gen.manual_seed(synth.CONFIG_SEED[2] + 201)
+    gen.manual_seed(synth.SEED_FULL_S8192 + 201)
     q, k, v, g = (dev_normal(gen, (T, 16, 256)), dev_normal(gen, (T, 4, 256)),
                   dev_normal(gen, (T, 4, 256)), dev_normal(gen, (T, 16)))
     o = torch.empty_like(q)
@@ -194,10 +194,10 @@ def bench_configs(fga, synth):
         log(f"varlen prefill {name}, 16 sequences (T={T}): {ms:.3f} ms  {tf:.0f} TFLOP/s")
     del q, k, v, g, o, ws, cu
 
-    # Config 4: 36-layer stack, batch 1, S = 32768, independent inputs per layer (drawn on
+    # The 36-layer stack, batch 1, S = 32768, independent inputs per layer (drawn on
     # the device: 24 GB of N(0,1) bf16); layer l is full iff l % 4 == 3.
     S = 32768
-    gen.manual_seed(synth.CONFIG_SEED[4])
+    gen.manual_seed(synth.SEED_STACK_S32768)
     layers = []
     for layer in range(36):
         layers.append(((fga.FULL if layer % 4 == 3 else fga.SLIDING),
@@ -215,7 +215,7 @@ def bench_configs(fga, synth):
     tf = flops / (ms * 1e-3) / 1e12
     out["stack36_prefill_s32768"] = {"ms": ms, "tflops": tf, "frac_mfma": tf / PEAK_BF16_TFLOPS,
                                      "tokens_per_s": S / (ms * 1e-3), "tflop": flops / 1e12}
-    log(f"config 4 36-layer stack S=32768: {ms:.2f} ms  {tf:.0f} TFLOP/s")
+    log(f"36-layer prefill stack S=32768: {ms:.2f} ms  {tf:.0f} TFLOP/s")
     del layers, ws
     torch.cuda.empty_cache()
 
@@ -244,27 +244,27 @@ def bench_configs(fga, synth):
                 "frac_hbm": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, "bytes": nbytes,
                 "cache": "cold" if cold else "warm"}
 
-    # Config 3: batch 64, lengths uniform in [1024, 32768].
-    seed = synth.CONFIG_SEED[3]
+    # Batched decode: batch 64, lengths uniform in [1024, 32768].
+    seed = synth.SEED_DECODE_B64
     lens = synth.decode_seq_lens(seed, 64, 1024, 32768)
     r = decode_case(fga.FULL, 64, lens, 32768, seed, cold=True)
     out["decode_b64_full_cold"] = r
-    log(f"config 3 decode full, cold: {r['us']:.0f} us  {r['gbs']:.0f} GB/s")
+    log(f"decode B=64 full, cold: {r['us']:.0f} us  {r['gbs']:.0f} GB/s")
     torch.cuda.empty_cache()
     for cold in (False, True):
         r = decode_case(fga.SLIDING, 64, lens, 512, seed + 1, cold=cold)
         out[f"decode_b64_sliding_{r['cache']}"] = r
-        log(f"config 3 decode sliding ring, {r['cache']}: {r['us']:.1f} us  {r['gbs']:.0f} GB/s")
+        log(f"decode B=64 sliding ring, {r['cache']}: {r['us']:.1f} us  {r['gbs']:.0f} GB/s")
 
-    # Config 5: long decode, full layer (cache capacity = L) and the sliding ring.
+    # Long decode (B = 4 at 131072 tokens, B = 1 at 2^20), full layer (cache capacity = L) and the sliding ring.
     for B, L in ((4, 131072), (1, 1 << 20)):
-        r = decode_case(fga.FULL, B, [L] * B, L, synth.CONFIG_SEED[5] + B, cold=True)
+        r = decode_case(fga.FULL, B, [L] * B, L, synth.SEED_LONG_DECODE + B, cold=True)
         out[f"decode_full_b{B}_l{L}_cold"] = r
-        log(f"config 5 decode full B={B} L={L}, cold: {r['us']:.0f} us  {r['gbs']:.0f} GB/s")
+        log(f"long decode full B={B} L={L}, cold: {r['us']:.0f} us  {r['gbs']:.0f} GB/s")
         torch.cuda.empty_cache()
-        r = decode_case(fga.SLIDING, B, [L] * B, 512, synth.CONFIG_SEED[5] + 10 + B, cold=True)
+        r = decode_case(fga.SLIDING, B, [L] * B, 512, synth.SEED_LONG_DECODE + 10 + B, cold=True)
         out[f"decode_sliding_b{B}_l{L}_cold"] = r
-        log(f"config 5 decode sliding B={B} L={L}, cold: {r['us']:.1f} us")
+        log(f"long decode sliding B={B} L={L}, cold: {r['us']:.1f} us")
     # 8-bit (q8_0) cache: 272 bytes per key row and KV head for K and for V, instead of 512.
     def decode_q8_case(lt, B, lens, cap, seed, cold):
         lens = np.asarray(lens, dtype=np.int32)
@@ -286,25 +286,25 @@ def bench_configs(fga, synth):
                 "frac_hbm": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, "bytes": nbytes,
                 "cache": "cold" if cold else "warm", "kv": "q8_0"}
 
-    seed = synth.CONFIG_SEED[3]
+    seed = synth.SEED_DECODE_B64
     lens = synth.decode_seq_lens(seed, 64, 1024, 32768)
     r = decode_q8_case(fga.FULL, 64, lens, 32768, seed + 50, cold=True)
     out["decode_q8_b64_full_cold"] = r
-    log(f"config 3 decode q8 full, cold: {r['us']:.0f} us  {r['gbs']:.0f} GB/s")
+    log(f"decode q8 B=64 full, cold: {r['us']:.0f} us  {r['gbs']:.0f} GB/s")
     torch.cuda.empty_cache()
     r = decode_q8_case(fga.SLIDING, 64, lens, 512, seed + 51, cold=True)
     out["decode_q8_b64_sliding_cold"] = r
-    log(f"config 3 decode q8 sliding ring, cold: {r['us']:.1f} us  {r['gbs']:.0f} GB/s")
+    log(f"decode q8 B=64 sliding ring, cold: {r['us']:.1f} us  {r['gbs']:.0f} GB/s")
     for B, L in ((4, 131072), (1, 1 << 20)):
-        r = decode_q8_case(fga.FULL, B, [L] * B, L, synth.CONFIG_SEED[5] + 60 + B, cold=True)
+        r = decode_q8_case(fga.FULL, B, [L] * B, L, synth.SEED_LONG_DECODE + 60 + B, cold=True)
         out[f"decode_q8_full_b{B}_l{L}_cold"] = r
-        log(f"config 5 decode q8 full B={B} L={L}, cold: {r['us']:.0f} us  {r['gbs']:.0f} GB/s")
+        log(f"long decode q8 full B={B} L={L}, cold: {r['us']:.0f} us  {r['gbs']:.0f} GB/s")
         torch.cuda.empty_cache()
     # One decode step of the whole 36-layer model: batch 64, lengths uniform in [1024, 32768]
     # (each layer its own cache: 9 full caches, 27 rings), bf16 and 8-bit caches.
     del flush_a
     torch.cuda.empty_cache()
-    seed = synth.CONFIG_SEED[3]
+    seed = synth.SEED_DECODE_B64
     lens = synth.decode_seq_lens(seed, 64, 1024, 32768)
     sl = torch.as_tensor(lens).cuda()
     maxlen = int(lens.max())
@@ -347,7 +347,7 @@ def bench_configs(fga, synth):
     # The W8A8 FP8 q/k/v projection with the bf16 gate projection upstream of the path:
     # T tokens of hidden 2560 -> 6144 q/k/v channels (+ 16 gate logits).
     for T in (8192, 32768):
-        gen.manual_seed(synth.CONFIG_SEED[1] + 400 + T)
+        gen.manual_seed(synth.SEED_SLIDING_S1024 + 400 + T)
         x = dev_normal(gen, (T, 2560))
         w = torch.randint(0x18, 0x50, (6144, 2560), generator=gen, device="cuda", dtype=torch.uint8)
         w = torch.where(torch.rand(w.shape, generator=gen, device="cuda") < 0.5, w, w | 0x80)
@@ -412,7 +412,7 @@ def cpu_baseline(synth, budget_s=12.0, S=8192):
         threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
     except Exception:  # pragma: no cover
         threads = len(os.sched_getaffinity(0))
-    inp = synth.prefill_inputs(synth.CONFIG_SEED[2], 1, S)
+    inp = synth.prefill_inputs(synth.SEED_FULL_S8192, 1, S)
     rng = np.random.default_rng(12345)
     rows_done = 0
     t0 = time.perf_counter()

@@ -26,8 +26,12 @@ N_KV_HEADS = 4
 HEAD_DIM = 256
 BLOCK = 1 << 22
 
-# Seeds of the five workloads and of the 36-layer stack.
-CONFIG_SEED = {1: 20261, 2: 20262, 3: 20263, 4: 20264, 5: 20265}
+# Seeds of the measured workloads (each tensor then takes its own stream below them).
+SEED_SLIDING_S1024 = 20261   # one sliding layer, batch 1, S = 1024
+SEED_FULL_S8192 = 20262      # one full layer, batch 1, S = 8192
+SEED_DECODE_B64 = 20263      # batched decode, batch 64, lengths uniform in [1024, 32768]
+SEED_STACK_S32768 = 20264    # the 36-layer prefill stack, S = 32768 (times 1000 plus the layer)
+SEED_LONG_DECODE = 20265     # decode at 131072 tokens (batch 4) and 2^20 (batch 1)
 
 
 def _threads() -> int:
@@ -85,7 +89,7 @@ def prefill_inputs(seed: int, batch: int, seq: int) -> dict:
 
 def stack_layer_seed(layer: int) -> int:
     """Seed of layer ``layer`` (0-based) of the 36-layer prefill stack."""
-    return CONFIG_SEED[4] * 1000 + layer
+    return SEED_STACK_S32768 * 1000 + layer
 
 
 def decode_seq_lens(seed: int, batch: int, lo: int, hi: int) -> np.ndarray:

@@ -87,13 +87,13 @@ def test_decode_zero_length_sequences(fga, num_parts):
     assert_parity(got[live], want, f"decode with empty sequences parts={num_parts}")
 
 
-def test_config3_batched_decode(fga):
+def test_batched_decode_b64(fga):
     """Batch 64, context lengths uniform in [1024, 32768]; full cache and 512-slot ring."""
     import torch
-    seed = synth.CONFIG_SEED[3]
+    seed = synth.SEED_DECODE_B64
     B, cap = 64, 32768
     lens = synth.decode_seq_lens(seed, B, 1024, 32768)
-    note(f"config3 lens sum={int(lens.sum())}")
+    note(f"decode B=64 lens sum={int(lens.sum())}")
     q = synth.normal_bf16(seed, 0, (B, 16, 256))
     gate = synth.normal_bf16(seed, 1, (B, 16))
     cache = fga.KVCache(oracle.FULL, B, cap)
@@ -107,21 +107,21 @@ def test_config3_batched_decode(fga):
     out = fga.decode(oracle.FULL, to_dev(q), to_dev(gate), cache, i32_dev(lens), cap)
     torch.cuda.synchronize()
     want = oracle.decode(q, gate, host_k, host_v, lens, oracle.FULL)
-    assert_parity(f64_of(out), want, "config3 full")
+    assert_parity(f64_of(out), want, "decode B=64 full")
     rk, rv = _ring_from_contiguous(host_k, host_v, lens)
     del cache
     ring = fga.KVCache(oracle.SLIDING, B, 512, k=to_dev(rk), v=to_dev(rv))
     out = fga.decode(oracle.SLIDING, to_dev(q), to_dev(gate), ring, i32_dev(lens), cap)
     torch.cuda.synchronize()
     want = oracle.decode(q, gate, rk, rv, lens, oracle.SLIDING)
-    assert_parity(f64_of(out), want, "config3 sliding")
+    assert_parity(f64_of(out), want, "decode B=64 sliding")
 
 
 @pytest.mark.parametrize("B,L", [(4, 131072), (1, 1048576)], ids=["B4_L131072", "B1_L1048576"])
-def test_config5_long_decode(fga, B, L):
+def test_long_decode(fga, B, L):
     """Long-context decode on a full layer (cache capacity = L) and on the sliding ring."""
     import torch
-    seed = synth.CONFIG_SEED[5] + B
+    seed = synth.SEED_LONG_DECODE + B
     lens = np.full(B, L, np.int32)
     q = synth.normal_bf16(seed, 0, (B, 16, 256))
     gate = synth.normal_bf16(seed, 1, (B, 16))
@@ -132,18 +132,18 @@ def test_config5_long_decode(fga, B, L):
         host_k[b], host_v[b] = synth.cache_rows(seed, b, L)
         cache.k[b] = to_dev(host_k[b])
         cache.v[b] = to_dev(host_v[b])
-    note(f"config5 B={B} L={L} uploaded")
+    note(f"long decode B={B} L={L} uploaded")
     out = fga.decode(oracle.FULL, to_dev(q), to_dev(gate), cache, i32_dev(lens), L)
     torch.cuda.synchronize()
     want = oracle.decode(q, gate, host_k, host_v, lens, oracle.FULL)
-    assert_parity(f64_of(out), want, f"config5 full B={B} L={L}")
+    assert_parity(f64_of(out), want, f"long decode full B={B} L={L}")
     rk, rv = _ring_from_contiguous(host_k, host_v, lens)
     del cache
     ring = fga.KVCache(oracle.SLIDING, B, 512, k=to_dev(rk), v=to_dev(rv))
     out = fga.decode(oracle.SLIDING, to_dev(q), to_dev(gate), ring, i32_dev(lens), L)
     torch.cuda.synchronize()
     want = oracle.decode(q, gate, rk, rv, lens, oracle.SLIDING)
-    assert_parity(f64_of(out), want, f"config5 sliding B={B} L={L}")
+    assert_parity(f64_of(out), want, f"long decode sliding B={B} L={L}")
 
 
 APPEND = [(oracle.FULL, 1, [0, 7]), (oracle.FULL, 33, [0, 100]), (oracle.SLIDING, 5, [0, 1000]),

@@ -40,12 +40,12 @@ def test_prefill_small_all_rows(fga, lt, B, S):
     assert_parity(got, want, f"prefill lt={lt} B={B} S={S}")
 
 
-def test_config1_sliding_s1024_all_rows(fga):
+def test_sliding_s1024_all_rows(fga):
     """Single sliding-window layer, batch 1, S=1024, theta 1e4 over all 256 dims."""
-    inp = synth.prefill_inputs(synth.CONFIG_SEED[1], 1, 1024)
+    inp = synth.prefill_inputs(synth.SEED_SLIDING_S1024, 1, 1024)
     got = f64_of(_run(fga, inp, oracle.SLIDING))
     want = oracle.prefill(inp["q"], inp["k"], inp["v"], inp["gate"], oracle.SLIDING)
-    assert_parity(got, want, "config1 sliding S=1024")
+    assert_parity(got, want, "sliding S=1024")
 
 
 def _sample_rows(S, seed, n_random):
@@ -54,18 +54,18 @@ def _sample_rows(S, seed, n_random):
     return np.unique(np.concatenate([fixed, rnd]))
 
 
-def test_config2_full_s8192_sampled_rows(fga):
+def test_full_s8192_sampled_rows(fga):
     """Single full layer, batch 1, S=8192, theta 5e6 on the first 64 dims: 256 sampled rows."""
     S = 8192
-    inp = synth.prefill_inputs(synth.CONFIG_SEED[2], 1, S)
+    inp = synth.prefill_inputs(synth.SEED_FULL_S8192, 1, S)
     got = f64_of(_run(fga, inp, oracle.FULL))
-    rows = _sample_rows(S, synth.CONFIG_SEED[2] + 1, 247)
+    rows = _sample_rows(S, synth.SEED_FULL_S8192 + 1, 247)
     want = oracle.prefill(inp["q"], inp["k"], inp["v"], inp["gate"], oracle.FULL, rows=rows)
-    assert_parity(got[:, rows], want, "config2 full S=8192 sampled rows")
+    assert_parity(got[:, rows], want, "full S=8192 sampled rows")
 
 
 @pytest.mark.parametrize("layer", list(range(36)))
-def test_config4_stack_layer_s32768_sampled_rows(fga, layer):
+def test_stack_layer_s32768_sampled_rows(fga, layer):
     """36-layer stack, batch 1, S=32768, independent inputs per layer: 64 sampled rows each."""
     S = 32768
     lt = oracle.layer_type_of(layer)
@@ -75,7 +75,7 @@ def test_config4_stack_layer_s32768_sampled_rows(fga, layer):
     rows = _sample_rows(S, synth.stack_layer_seed(layer) + 1, 55)
     got = f64_of(got[:, rows])
     want = oracle.prefill(inp["q"], inp["k"], inp["v"], inp["gate"], lt, rows=rows)
-    assert_parity(got, want, f"config4 layer {layer} lt={lt}")
+    assert_parity(got, want, f"stack S=32768 layer {layer} lt={lt}")
 
 
 @pytest.mark.parametrize("lt", [oracle.SLIDING, oracle.FULL], ids=["sliding", "full"])

@@ -130,26 +130,26 @@ def test_decode_q8_edges(fga, lens, num_parts):
     assert_parity(got, want, f"decode q8 sliding lens={lens.tolist()} parts={num_parts}")
 
 
-def test_decode_q8_config3(fga):
+def test_decode_q8_b64(fga):
     """Batch 64, context lengths uniform in [1024, 32768]: full cache and 512-slot ring."""
-    seed = synth.CONFIG_SEED[3]
+    seed = synth.SEED_DECODE_B64
     B, cap = 64, 32768
     lens = synth.decode_seq_lens(seed, B, 1024, 32768)
     q = synth.normal_bf16(seed, 0, (B, 16, 256))
     gate = synth.normal_bf16(seed, 1, (B, 16))
     arrays = _cache_arrays(seed + 7, B, cap, fill_lens=lens)
-    note("decode q8 config3 full")
+    note("decode q8 B=64 full")
     got = _decode_q8(fga, oracle.FULL, q, gate, arrays, lens, max_len=cap)
-    assert_parity(got, oracle.decode_q8(q, gate, *arrays, lens, oracle.FULL), "decode q8 config3 full")
+    assert_parity(got, oracle.decode_q8(q, gate, *arrays, lens, oracle.FULL), "decode q8 B=64 full")
     ring = _ring_of(arrays, lens)
     del arrays
     got = _decode_q8(fga, oracle.SLIDING, q, gate, ring, lens, max_len=cap)
-    assert_parity(got, oracle.decode_q8(q, gate, *ring, lens, oracle.SLIDING), "decode q8 config3 sliding")
+    assert_parity(got, oracle.decode_q8(q, gate, *ring, lens, oracle.SLIDING), "decode q8 B=64 sliding")
 
 
 def test_decode_q8_long(fga):
     """Batch 4 at 131072 tokens on a full layer, and their 512-slot rings."""
-    seed = synth.CONFIG_SEED[5] + 40
+    seed = synth.SEED_LONG_DECODE + 40
     B, L = 4, 131072
     lens = np.full(B, L, np.int32)
     q = synth.normal_bf16(seed, 0, (B, 16, 256))
