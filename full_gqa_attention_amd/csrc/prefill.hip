@@ -584,23 +584,34 @@ void prefill_kernel(PrefillArgs a) {
       __builtin_amdgcn_wave_barrier();
     }
   } else {
+    // Full layers: lanes l and l + 32 hold the two 4-dim halves of each 8-dim run of row
+    // l % 32; one v_permlane32_swap per dword gives lane l the whole even run and lane l + 32
+    // the whole odd run of each pair, so every store writes 16 contiguous bytes (half as
+    // many row-scattered store instructions as 8-byte pieces would need).
 #pragma unroll
     for (int rb = 0; rb < kRowBlocks; ++rb) {
       const int row = q0 + 32 * (rb0 + rb) + r32;
       const float l_tot = l_part[rb] + __shfl_xor(l_part[rb], 32);
-      if (row < S) {
-        const float gl = bf16_to_f32(a.gate[(sp.row0 + row) * kQHeads + hq]);
-        const float scale = sigmoidf_fast(gl) / l_tot;
-        uint16_t* orow = a.out + ((sp.row0 + row) * kQHeads + hq) * kHeadDim;
+      const bool ok = row < S;                 // the same for lanes l and l + 32
+      const float gl = ok ? bf16_to_f32(a.gate[(sp.row0 + row) * kQHeads + hq]) : 0.0f;
+      const float scale = sigmoidf_fast(gl) / l_tot;
+      uint16_t* orow = a.out + ((sp.row0 + (ok ? row : 0)) * kQHeads + hq) * kHeadDim;
 #pragma unroll
-        for (int db = 0; db < 8; ++db) {
+      for (int db = 0; db < 8; ++db) {
 #pragma unroll
-          for (int qd = 0; qd < 4; ++qd) {
-            u32x2 w;
-            w[0] = pack_bf16x2(o[rb][db][4 * qd] * scale, o[rb][db][4 * qd + 1] * scale);
-            w[1] = pack_bf16x2(o[rb][db][4 * qd + 2] * scale, o[rb][db][4 * qd + 3] * scale);
-            *reinterpret_cast<u32x2*>(orow + 32 * db + 8 * qd + 4 * half) = w;
-          }
+        for (int m = 0; m < 2; ++m) {
+          // Elements 8m .. 8m + 3 are run qd = 2m, 8m + 4 .. 8m + 7 run 2m + 1.
+          const f32x16& ov = o[rb][db];
+          const uint32_t e0 = pack_bf16x2(ov[8 * m] * scale, ov[8 * m + 1] * scale);
+          const uint32_t e1 = pack_bf16x2(ov[8 * m + 2] * scale, ov[8 * m + 3] * scale);
+          const uint32_t d0 = pack_bf16x2(ov[8 * m + 4] * scale, ov[8 * m + 5] * scale);
+          const uint32_t d1 = pack_bf16x2(ov[8 * m + 6] * scale, ov[8 * m + 7] * scale);
+          // Lanes < 32 keep e and receive e of lane + 32; lanes >= 32 receive d of lane - 32
+          // and keep d: each then holds dims 8 (2m + half) .. + 7 in order.
+          const auto s0 = __builtin_amdgcn_permlane32_swap(e0, d0, false, false);
+          const auto s1 = __builtin_amdgcn_permlane32_swap(e1, d1, false, false);
+          if (ok)
+            *reinterpret_cast<u32x4*>(orow + 32 * db + 8 * (2 * m + half)) = u32x4{s0[0], s1[0], s0[1], s1[1]};
         }
       }
     }
