@@ -111,16 +111,22 @@ __device__ __forceinline__ void attend_segment(const DecodeArgs& a, int b, int L
   const size_t seq_base = (size_t)b * a.cache_cap * kSlot + (size_t)g * kHeadDim;
   const uint16_t* kbase = a.cache_k + seq_base;
   const uint16_t* vbase = a.cache_v + seq_base;
-  const int vpar = lane >> 5;           // key parity this lane accumulates
-  const int vdim = 8 * (lane & 31);     // first of the 8 dims this lane owns
+  // PV: bf16 -- lane owns 8 dims of the keys of one parity (two 512-byte rows per load);
+  // 8-bit -- lane owns 16 dims (half a quantisation block) of the keys c0 + 4i + l / 16
+  // (four 256-byte code rows per 16-byte load, one scale per key).
+  constexpr int kVDims = Q8 ? 16 : 8;
+  constexpr int kVStep = kVDims / 4;                    // keys per load instruction
+  constexpr int kVKeys = kChunk / kVStep;               // keys per lane and chunk
+  const int vpar = Q8 ? lane >> 4 : lane >> 5;          // key residue this lane accumulates
+  const int vdim = kVDims * (Q8 ? lane & 15 : lane & 31);   // first of the dims this lane owns
 
-  float m_run[4], l_run[4], acc[4][8];
+  float m_run[4], l_run[4], acc[4][kVDims];
 #pragma unroll
   for (int h = 0; h < 4; ++h) {
     m_run[h] = -1e30f;
     l_run[h] = 0.0f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[h][e] = 0.0f;
+    for (int e = 0; e < kVDims; ++e) acc[h][e] = 0.0f;
   }
 
   // 8-bit cache: codes at the same element offsets (one byte each); scales [slot][4][8].
@@ -155,17 +161,16 @@ __device__ __forceinline__ void attend_segment(const DecodeArgs& a, int b, int L
         }
       }
     }
-    u32x4 vr[16];
-    u32x2 vr8[16];
-    float vsc[16];
+    u32x4 vr[kVKeys];
+    float vsc[kVKeys];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int key = c0 + 2 * i + vpar;
+    for (int i = 0; i < kVKeys; ++i) {
+      const int key = c0 + kVStep * i + vpar;
       const bool ok = key < ke;
       const size_t row = (size_t)(ok ? key : ks);
       if constexpr (Q8) {
         // As for K: a row past the segment gets P = 0, so its finite values add nothing.
-        vr8[i] = *reinterpret_cast<const u32x2*>(vbase8 + ((uint32_t)row * kSlot + vdim));
+        vr[i] = *reinterpret_cast<const u32x4*>(vbase8 + ((uint32_t)row * kSlot + vdim));
         vsc[i] = half_to_f32(vscale[(uint32_t)row * (kKvHeads * 8) + (vdim >> 5)]);
       } else {
         const u32x4 x = ld_global16(vbase + row * kSlot + vdim);
@@ -225,15 +230,15 @@ __device__ __forceinline__ void attend_segment(const DecodeArgs& a, int b, int L
 #pragma unroll
     for (int h = 0; h < 4; ++h)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[h][e] *= al[h];
+      for (int e = 0; e < kVDims; ++e) acc[h][e] *= al[h];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      f32x4 pp = *reinterpret_cast<const f32x4*>(&s_p[g][2 * i + vpar][0]);
-      float x[8];
+    for (int i = 0; i < kVKeys; ++i) {
+      f32x4 pp = *reinterpret_cast<const f32x4*>(&s_p[g][kVStep * i + vpar][0]);
+      float x[kVDims];
       if constexpr (Q8) {
         pp *= vsc[i];                          // value = code * scale: fold the scale into P
 #pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = (float)(int8_t)((vr8[i][e >> 2] >> (8 * (e & 3))) & 0xff);
+        for (int e = 0; e < 16; ++e) x[e] = (float)(int8_t)((vr[i][e >> 2] >> (8 * (e & 3))) & 0xff);
       } else {
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
@@ -244,24 +249,29 @@ __device__ __forceinline__ void attend_segment(const DecodeArgs& a, int b, int L
 #pragma unroll
       for (int h = 0; h < 4; ++h)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[h][e] += pp[h] * x[e];
+        for (int e = 0; e < kVDims; ++e) acc[h][e] += pp[h] * x[e];
     }
     __builtin_amdgcn_wave_barrier();
   }
 
-  // Merge the two key parities, then write this segment's partial results.
+  // Merge the lanes that hold the same dims of other keys, then write this segment's
+  // partial results.
 #pragma unroll
   for (int h = 0; h < 4; ++h)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[h][e] += __shfl_xor(acc[h][e], 32);
+    for (int e = 0; e < kVDims; ++e) {
+      if constexpr (Q8) acc[h][e] += __shfl_xor(acc[h][e], 16);
+      acc[h][e] += __shfl_xor(acc[h][e], 32);
+    }
 
   const size_t head0 = (size_t)slot * kQHeads + g * kGroup;
-  if (lane < 32) {
+  if (lane < 256 / kVDims) {
 #pragma unroll
     for (int h = 0; h < 4; ++h) {
       float* dst = a.ws_o + (head0 + h) * kHeadDim + vdim;
-      *reinterpret_cast<f32x4*>(dst) = f32x4{acc[h][0], acc[h][1], acc[h][2], acc[h][3]};
-      *reinterpret_cast<f32x4*>(dst + 4) = f32x4{acc[h][4], acc[h][5], acc[h][6], acc[h][7]};
+#pragma unroll
+      for (int e = 0; e < kVDims; e += 4)
+        *reinterpret_cast<f32x4*>(dst + e) = f32x4{acc[h][e], acc[h][e + 1], acc[h][e + 2], acc[h][e + 3]};
     }
   }
   if (lane == 0) {
