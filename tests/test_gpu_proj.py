@@ -34,7 +34,8 @@ def _assert_close(got, want, what, sum_abs):
     err = np.abs(got - want)
     bound = 2.0 ** -8 * np.abs(want) + 2.0 ** -16 * sum_abs
     rel = float(np.linalg.norm(got - want) / np.linalg.norm(want))
-    ratio = err / bound
+    # A zero bound (an all-zero token: every term is 0) admits only an exact 0.
+    ratio = np.divide(err, bound, out=np.where(err > 0, np.inf, 0.0), where=bound > 0)
     wi = int(np.argmax(ratio))
     worst = float(ratio.flat[wi])
     note(f"[proj] {what}: max |err|/bound = {worst:.3f} (err {err.flat[wi]:.3e} at |y| = "
@@ -107,3 +108,34 @@ def test_projection_feeds_prefill(fga):
     from gpu_util import assert_parity, bits_of
     want = oracle.prefill(bits_of(q)[None], bits_of(k)[None], bits_of(v)[None], bits_of(g)[None], oracle.FULL)
     assert_parity(f64_of(out), want, "projection -> prefill")
+
+
+def test_qkv_proj_degenerate_tokens(fga):
+    """Tokens the per-token quantiser treats specially, in a batch of 260 (two GEMM row
+    tiles, the second ragged): an all-zero token (scale 0, codes 0, outputs 0), a token whose
+    only non-zero value is a large outlier, a constant token (every code +-448) and a token
+    of tiny values.  Codes and scales bit for bit, outputs to the usual bound."""
+    T = 260
+    inp = synth.proj_inputs(9400, T)
+    x = oracle.bf16_to_f64(inp["x"]).copy()
+    x[0] = 0.0
+    x[1] = 0.0
+    x[1, 1234] = 3.0e4
+    x[2] = -1.5
+    x[T - 1] *= 1e-20
+    inp["x"] = oracle.round_to_bf16_bits(x)
+    q, k, v, g, ws = _run(fga, inp)
+    codes, scales = oracle.quantize_tokens(inp["x"])
+    assert scales[0] == 0.0 and not codes[0].any()
+    assert np.all((codes[2] == 0xFE))
+    pad = (T * 2560 + 255) // 256 * 256
+    got_codes = ws[:T * 2560].reshape(T, 2560)
+    got_scales = ws[pad:pad + 4 * T].view(np.float32)
+    bad = np.argwhere(got_codes != codes)
+    assert bad.size == 0, f"activation codes differ at (token, k) {bad[:5].tolist()}"
+    assert np.array_equal(got_scales, scales), "activation scales differ"
+    wq, wk, wv, wg = oracle.qkv_proj(inp["x"], inp["w"], inp["w_scale"], inp["wg"])
+    assert not f64_of(q)[0].any() and not f64_of(g)[0].any(), "a zero token must project to zeros"
+    sq, sk, sv, sg = _sum_abs(inp)
+    for name, got, want, sa in zip(("q", "k", "v", "gate"), (q, k, v, g), (wq, wk, wv, wg), (sq, sk, sv, sg)):
+        _assert_close(f64_of(got), want, f"{name} degenerate tokens", sa)
