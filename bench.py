@@ -344,6 +344,35 @@ def bench_configs(fga, synth):
             f"{nbytes / (ms * 1e-3) / 1e9:.0f} GB/s")
         del layers
         torch.cuda.empty_cache()
+    # KV append: a bulk append of 32768 tokens (batch 1, full cache; the sliding ring keeps
+    # the last 512), and the one-token append of a batch-64 decode step at positions
+    # U[1024, 32768]; bf16 and 8-bit caches.  Bytes per written token: its K and V read
+    # (2 x 2 KB) plus what the cache receives (2 x 2 KB, or 2 x 1088 B for q8_0).
+    lens = synth.decode_seq_lens(synth.SEED_DECODE_B64, 64, 1024, 32768)
+    for kv in ("bf16", "q8_0"):
+        for lt, B, n in ((fga.FULL, 1, 32768), (fga.SLIDING, 1, 32768), (fga.FULL, 64, 1), (fga.SLIDING, 64, 1)):
+            gen.manual_seed(synth.SEED_DECODE_B64 + 500 + B)
+            cap = 512 if lt == fga.SLIDING else (32768 if B == 64 else n)
+            k = dev_normal(gen, (B, n, 4, 256))
+            v = dev_normal(gen, (B, n, 4, 256))
+            pos = torch.as_tensor(lens - 1 if B == 64 else np.zeros(B, np.int32)).to(torch.int32).cuda()
+            if kv == "bf16":
+                cache = fga.KVCache(lt, B, cap)
+                call = lambda: fga.kv_append(lt, k, v, pos, cache)
+            else:
+                cache = fga.KVCacheQ8(lt, B, cap)
+                call = lambda: fga.kv_append_q8(lt, k, v, pos, cache)
+            written = B * (min(n, 512) if lt == fga.SLIDING else n)
+            row = 2 * 4 * (512 if kv == "bf16" else 272)
+            nbytes = written * (2 * 4 * 512 + row)   # only the tokens it writes are read
+            ms = time_each(call, 30, 5)
+            name = f"kv_append_{kv}_{'full' if lt == fga.FULL else 'sliding'}_b{B}_n{n}"
+            out[name] = {"us": ms * 1e3, "gbs": nbytes / (ms * 1e-3) / 1e9,
+                         "frac_hbm": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, "bytes": nbytes}
+            log(f"kv append ({kv}) {'full' if lt == fga.FULL else 'sliding'} B={B} n={n}: {ms * 1e3:.1f} us  "
+                f"{nbytes / (ms * 1e-3) / 1e9:.0f} GB/s")
+            del cache, k, v
+    torch.cuda.empty_cache()
     # The W8A8 FP8 q/k/v projection with the bf16 gate projection upstream of the path:
     # T tokens of hidden 2560 -> 6144 q/k/v channels (+ 16 gate logits).
     for T in (8192, 32768):
