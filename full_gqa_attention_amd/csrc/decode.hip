@@ -420,9 +420,9 @@ int cu_count() {
 }  // namespace
 
 // Partitions chosen automatically: one per CU for the bf16 cache (above); two per CU for
-// the 8-bit cache, whose waves spend about twice the VALU time per byte (dequantisation)
-// and hold half the bytes in flight per load: a second workgroup per CU hides one's
-// waits behind the other's arithmetic (batch 64, 1K-32K keys: 774 -> 525 us).
+// the 8-bit cache, whose waves hold half the bytes in flight per load and issue more,
+// smaller loads per byte: a second workgroup per CU keeps more bytes in flight while the
+// other waits (batch 64, 1K-32K keys: 774 -> 525 us).
 DecodePlan plan_decode(int layer_type, int batch, int max_seq_len, int nparts, bool q8) {
   DecodePlan p{};
   const int n = layer_type == kFull ? max_seq_len : (max_seq_len < kWindow ? max_seq_len : kWindow);
