@@ -84,17 +84,17 @@ def test_qkv_proj_all_rows(fga, T):
     _assert_close(f64_of(g), wg, f"gate T={T}", sg)
 
 
-def test_qkv_proj_8192_sampled_rows(fga):
-    """The benchmark's shape, 8192 tokens: 96 sampled tokens against the oracle (tokens are
-    independent: quantisation and products are per token)."""
-    T = 8192
-    inp = synth.proj_inputs(9200, T)
+@pytest.mark.parametrize("T", [8192, 32768])
+def test_qkv_proj_sampled_rows(fga, T):
+    """The benchmark's shapes, 8192 and 32768 tokens: 96 sampled tokens against the oracle
+    (tokens are independent: quantisation and products are per token)."""
+    inp = synth.proj_inputs(9200 + T, T)
     q, k, v, g, _ = _run(fga, inp)
-    rows = np.unique(np.concatenate([[0, 127, 128, T - 1], np.random.default_rng(9201).choice(T, 92, replace=False)]))
+    rows = np.unique(np.concatenate([[0, 255, 256, T - 1], np.random.default_rng(9201).choice(T, 92, replace=False)]))
     wq, wk, wv, wg = oracle.qkv_proj(inp["x"][rows], inp["w"], inp["w_scale"], inp["wg"])
     sums = _sum_abs(inp, rows)
     for name, got, want, sa in zip(("q", "k", "v", "gate"), (q, k, v, g), (wq, wk, wv, wg), sums):
-        _assert_close(f64_of(got[rows]), want, f"{name} T=8192 sampled", sa)
+        _assert_close(f64_of(got[rows]), want, f"{name} T={T} sampled", sa)
 
 
 def test_projection_feeds_prefill(fga):
