@@ -107,3 +107,21 @@ def test_varlen_length_mix_sampled_rows(fga, lt):
     rows = np.array(rows)
     want = oracle.prefill_varlen(x["q"], x["k"], x["v"], x["gate"], cu, lt, rows=rows)
     assert_parity(f64_of(got[rows]), want, f"varlen mix lt={lt}")
+
+
+@pytest.mark.parametrize("lt", [oracle.SLIDING, oracle.FULL], ids=["sliding", "full"])
+def test_varlen_benchmark_mix_sampled_rows(fga, lt):
+    """The benchmark's batch: sixteen sequences of lengths uniform in [512, 8192] (the same
+    draw), 12 sampled rows per sequence, first and last included."""
+    lens = np.random.default_rng(synth.SEED_FULL_S8192 + 200).integers(512, 8193, size=16).tolist()
+    x, cu = _packed(8400 + lt, lens)
+    note(f"varlen benchmark mix lt={lt} T={int(cu[-1])}")
+    got = _run(fga, lt, x, cu, max(lens))
+    rng = np.random.default_rng(8401 + lt)
+    rows = []
+    for b, n in enumerate(lens):
+        pick = {0, n - 1} | set(rng.choice(n, size=10, replace=False).tolist())
+        rows += [int(cu[b]) + r for r in sorted(pick)]
+    rows = np.array(rows)
+    want = oracle.prefill_varlen(x["q"], x["k"], x["v"], x["gate"], cu, lt, rows=rows)
+    assert_parity(f64_of(got[rows]), want, f"varlen benchmark mix lt={lt}")
