@@ -40,6 +40,9 @@ namespace {
 constexpr int kThreads = 256;   // 4 waves = 4 KV heads
 constexpr int kChunk = 32;      // keys per inner iteration and per partition unit
 constexpr int kSlot = kKvHeads * kHeadDim;   // bf16 per cache slot
+// LDS pitch of a staged 8-bit K row: 256 code bytes + 16, so that the 8-byte fragment reads
+// of 16 keys x two 8-byte column groups (half a wave) fall on 64 distinct banks.
+constexpr int kK8Pitch = 272;
 
 template <int LT>
 __device__ __forceinline__ int visible_keys(int L, int cap) {
@@ -82,7 +85,8 @@ __device__ __forceinline__ bf16x8 codes_to_bf16(u32x2 x) {
 template <int LT, bool Q8>
 __device__ __forceinline__ void attend_segment(const DecodeArgs& a, int b, int L, int ks, int ke,
                                                int slot, int g, int lane, const double* s_inv,
-                                               float (*s_p)[kChunk][4], float (*s_alpha)[4]) {
+                                               float (*s_p)[kChunk][4], float (*s_alpha)[4],
+                                               uint8_t* s_k8) {
   // Q as the A operand: lane l holds head l % 16 (only 0..3 are real), dims 32s + 8(l/16) + j.
   const int hrow = lane & 15;
   const int kq = lane >> 4;
@@ -140,17 +144,34 @@ __device__ __forceinline__ void attend_segment(const DecodeArgs& a, int b, int L
     u32x4 kr[2][8];
     u32x2 kr8[2][8];
     u32x4 ksc[2];
+    if constexpr (Q8) {
+      // The chunk's K codes through LDS: eight 16-byte loads per lane (key 4i + l / 16,
+      // bytes 16 (l % 16) ..), then the 8-byte MFMA fragments read back.  A row past the
+      // segment reads its first key: finite, and masked below, so nothing needs zeroing.
+      u32x4 kg[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int key = c0 + 4 * i + (lane >> 4);
+        const uint32_t row = (uint32_t)(key < ke ? key : ks);
+        kg[i] = *reinterpret_cast<const u32x4*>(kbase8 + (row * kSlot + 16 * (lane & 15)));
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        *reinterpret_cast<u32x4*>(s_k8 + (4 * i + (lane >> 4)) * kK8Pitch + 16 * (lane & 15)) = kg[i];
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int s = 0; s < 8; ++s)
+          kr8[kb][s] = *reinterpret_cast<const u32x2*>(s_k8 + (16 * kb + hrow) * kK8Pitch + 32 * s + 8 * kq);
+    }
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       const int key = c0 + 16 * kb + hrow;
       const bool ok = key < ke;
       const size_t row = (size_t)(ok ? key : ks);
       if constexpr (Q8) {
-        // 32-bit offsets from the sequence's base (a row past the segment reads its first
-        // key: finite, and masked below, so nothing needs zeroing).
-        const uint32_t off = (uint32_t)row * kSlot + 8 * kq;
-#pragma unroll
-        for (int s = 0; s < 8; ++s) kr8[kb][s] = *reinterpret_cast<const u32x2*>(kbase8 + (off + 32 * s));
+        // Scales straight from global memory; the codes come from the LDS stage below.
         ksc[kb] = ld_global16(kscale + (uint32_t)row * (kKvHeads * 8));
       } else {
         const uint16_t* src = kbase + row * kSlot + 8 * kq;
@@ -289,6 +310,8 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
   __shared__ double s_inv[T::kRot / 2];
   __shared__ __attribute__((aligned(16))) float s_p[kKvHeads][kChunk][4];
   __shared__ __attribute__((aligned(16))) float s_alpha[kKvHeads][4];
+  // 8-bit cache: each wave's chunk of K codes, 32 rows at a 272-byte pitch.
+  __shared__ __attribute__((aligned(16))) uint8_t s_k8[Q8 ? kKvHeads : 1][Q8 ? kChunk * kK8Pitch : 16];
 
   __shared__ int s_scan[kThreads];
 
@@ -346,7 +369,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
     if (cn > lo && cn > cb) {
       const int ks = (max(lo, cb) - cb) * kChunk;
       const int ke = min((min(hi, cn) - cb) * kChunk, n);
-      attend_segment<LT, Q8>(a, b, L, ks, ke, w + b, g, lane, s_inv, s_p, s_alpha);
+      attend_segment<LT, Q8>(a, b, L, ks, ke, w + b, g, lane, s_inv, s_p, s_alpha, &s_k8[Q8 ? g : 0][0]);
     }
     if (cn >= hi || b + 1 >= a.batch) break;
     ++b;
