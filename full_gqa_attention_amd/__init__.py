@@ -81,6 +81,11 @@ def _load():
     lib.spark_status_string.restype = ctypes.c_char_p
     lib.spark_abi_version.argtypes = []
     lib.spark_abi_version.restype = i32
+    lib.spark_layer_type_of.argtypes = [i32]
+    lib.spark_layer_type_of.restype = i32
+    lib.spark_layer_params.argtypes = [i32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i32),
+                                       ctypes.POINTER(i32)]
+    lib.spark_layer_params.restype = i32
     return lib
 
 
@@ -91,7 +96,7 @@ EXPORTED = ("spark_attn_prefill_workspace_bytes", "spark_attn_prefill", "spark_a
             "spark_attn_prefill_varlen", "spark_qkv_proj_fp8_workspace_bytes", "spark_qkv_proj_fp8",
             "spark_kv_append", "spark_attn_decode_workspace_bytes",
             "spark_attn_decode", "spark_kv_append_q8", "spark_attn_decode_q8_workspace_bytes", "spark_attn_decode_q8", "spark_status_string",
-            "spark_abi_version")
+            "spark_abi_version", "spark_layer_type_of", "spark_layer_params")
 
 
 def abi_version() -> int:
@@ -387,5 +392,17 @@ def decode_q8(layer_type: int, q, gate, cache: KVCacheQ8, seq_lens, max_seq_len:
 
 
 def layer_type_of(layer: int) -> int:
-    """Stack schedule: three sliding layers then one full layer, 9 times (last layer full)."""
-    return FULL if layer % 4 == 3 else SLIDING
+    """spark_layer_type_of: type of 0-based layer ``layer`` of the 36-layer stack."""
+    lt = int(_lib.spark_layer_type_of(int(layer)))
+    if lt < 0:
+        raise ValueError(f"layer {layer} is outside the {N_LAYERS}-layer stack")
+    return lt
+
+
+def layer_params(layer_type: int):
+    """spark_layer_params: (RoPE theta, rotated dims, window or None) of a layer type."""
+    th, rd, w = ctypes.c_double(), ctypes.c_int32(), ctypes.c_int32()
+    st = _lib.spark_layer_params(int(layer_type), ctypes.byref(th), ctypes.byref(rd), ctypes.byref(w))
+    if st:
+        raise SparkError(st, "spark_layer_params")
+    return th.value, rd.value, (w.value or None)

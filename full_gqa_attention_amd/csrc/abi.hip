@@ -78,6 +78,20 @@ extern "C" {
 
 int32_t spark_abi_version(void) { return SPARK_ATTN_ABI_VERSION; }
 
+int32_t spark_layer_type_of(int32_t layer) {
+  if (layer < 0 || layer >= SPARK_N_LAYERS) return -1;
+  return layer % 4 == 3 ? SPARK_LAYER_FULL : SPARK_LAYER_SLIDING;
+}
+
+int32_t spark_layer_params(int32_t layer_type, double* rope_theta, int32_t* rotary_dims, int32_t* window) {
+  if (!valid_type(layer_type)) return SPARK_ERR_INVALID_ARG;
+  const bool full = layer_type == SPARK_LAYER_FULL;
+  if (rope_theta) *rope_theta = full ? spark::LayerTraits<spark::kFull>::kTheta : spark::LayerTraits<spark::kSliding>::kTheta;
+  if (rotary_dims) *rotary_dims = full ? spark::LayerTraits<spark::kFull>::kRot : spark::LayerTraits<spark::kSliding>::kRot;
+  if (window) *window = full ? 0 : spark::kWindow;
+  return SPARK_OK;
+}
+
 const char* spark_status_string(int32_t s) {
   switch (s) {
     case SPARK_OK: return "ok";

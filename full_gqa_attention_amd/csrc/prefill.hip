@@ -37,7 +37,7 @@ namespace {
 
 constexpr int kBM = 64;            // query positions per workgroup
 constexpr int kBN = 32;            // keys per tile
-constexpr int kWaves = 8;                          // waves per workgroup (4 or 8)
+constexpr int kWaves = 8;                          // waves per workgroup
 constexpr int kRowBlocks = 8 / kWaves;            // 32-row blocks per wave
 constexpr int kThreads = 64 * kWaves;
 constexpr int kTileBytes = kBN * kHeadDim * 2;   // 16 KB per K or V tile

@@ -267,11 +267,9 @@ __global__ __launch_bounds__(64 * WM * WN) void qkv_gemm_kernel(ProjArgs a) {
   }
 }
 
-#ifndef SPARK_GEMM_CFG
-#define SPARK_GEMM_CFG 4, 2, 2, 4, 2, 128
-#endif
-#define SPARK_GEMM_KERNEL qkv_gemm_kernel<SPARK_GEMM_CFG>
-using GemmCfg = GemmShape<SPARK_GEMM_CFG>;
+// 256 x 256 workgroup tiles on 4 x 2 waves of 2 x 4 blocks, two 128-byte stages.
+using GemmCfg = GemmShape<4, 2, 2, 4, 2, 128>;
+#define SPARK_GEMM_KERNEL qkv_gemm_kernel<4, 2, 2, 4, 2, 128>
 
 }  // namespace
 

@@ -44,9 +44,10 @@
 extern "C" {
 #endif
 
-#define SPARK_ATTN_ABI_VERSION 7
+#define SPARK_ATTN_ABI_VERSION 8
 
-enum { SPARK_Q_HEADS = 16, SPARK_KV_HEADS = 4, SPARK_HEAD_DIM = 256, SPARK_WINDOW = 512 };
+enum { SPARK_Q_HEADS = 16, SPARK_KV_HEADS = 4, SPARK_HEAD_DIM = 256, SPARK_WINDOW = 512,
+       SPARK_N_LAYERS = 36 };
 
 typedef enum spark_layer_type {
   SPARK_LAYER_SLIDING = 0,
@@ -60,6 +61,26 @@ typedef enum spark_status {
   SPARK_ERR_WORKSPACE = 3,   /* workspace smaller than required                      */
   SPARK_ERR_HIP = 4          /* the HIP runtime reported a launch failure            */
 } spark_status;
+
+/*
+ * Type of 0-based layer `layer` of the 36-layer stack: three sliding-window layers, then one
+ * full-attention layer, nine times over, so the last layer (35) is full (Spark-X2.6-4B-Base
+ * hybrid attention explainer, eliteato.com/news/34565, section "36 层混合注意力排布";
+ * Spark-X2.6-4B config.json guide, lqnn.cn/news/248463, section "混合注意力").
+ * Returns SPARK_LAYER_FULL when layer mod 4 == 3, SPARK_LAYER_SLIDING for the other layers
+ * of 0..35, and -1 for a layer outside 0..35.  Pure function of its argument.
+ */
+int32_t spark_layer_type_of(int32_t layer);
+
+/*
+ * RoPE base, rotated width and window of a layer type (explainer page, parameter table of
+ * section "全局注意力 5M 基频 RoPE", and section "滑动窗口 512"): SLIDING 1e4, 256 dims,
+ * window 512; FULL 5e6, the first 64 dims (partial_rotary_factor 0.25), no window
+ * (*window = 0).  Any output pointer may be NULL.  SPARK_ERR_INVALID_ARG for an unknown
+ * type, with nothing written.
+ */
+int32_t spark_layer_params(int32_t layer_type, double* rope_theta, int32_t* rotary_dims,
+                           int32_t* window);
 
 /*
  * KV cache of one layer, for `batch` sequences.  The keys are stored after RoPE, the
@@ -85,7 +106,13 @@ typedef struct spark_kv_cache {
 size_t spark_attn_prefill_workspace_bytes(int32_t layer_type, int32_t batch, int32_t seq_len);
 
 /*
- * Prefill: attention of a chunk of `seq_len` new tokens per sequence, one layer, over
+ * Prefill of one layer (Spark-X2.6-4B-Base hybrid attention explainer, eliteato.com/news/34565:
+ * masks per layer type in section "36 层混合注意力排布", the 512-token band in "滑动窗口 512",
+ * RoPE per type in "全局注意力 5M 基频 RoPE", GQA and the head gate in "配套效率设计"; fp32
+ * softmax and the sigmoid gate: Spark X2.5-4B F16 vs Q4 comparison, hotelren.com/news/5475707,
+ * section 三).
+ *
+ * Attention of a chunk of `seq_len` new tokens per sequence, one layer, over
  * the chunk itself and, when start_pos > 0, over the start_pos earlier tokens already
  * in the cache (chunked prefill).  Token t of a sequence sits at position start_pos + t
  * and sees the keys at positions <= start_pos + t (SLIDING: the last 512 of them).
@@ -150,7 +177,10 @@ spark_status spark_qkv_proj_fp8(int32_t tokens, const void* x, const void* w_qkv
 size_t spark_attn_prefill_varlen_workspace_bytes(int32_t layer_type, int32_t total_tokens);
 
 /*
- * Prefill of a batch of sequences of different lengths, packed one after another
+ * Prefill of a variable-length batch: the masks, RoPE and gate of spark_attn_prefill (same
+ * passages of the hybrid attention explainer), applied to each sequence on its own.
+ *
+ * Sequences of different lengths are packed one after another
  * (variable-length batch): sequence b owns token rows cu_seqlens[b] .. cu_seqlens[b+1]-1
  * and its token t sits at position t; each sequence attends only to itself.
  *   cu_seqlens   device int32 [batch + 1]: 0 = cu[0] <= cu[1] <= ... <= cu[batch] =
@@ -179,6 +209,11 @@ spark_status spark_attn_prefill_varlen(int32_t layer_type, int32_t batch, const 
                                        size_t workspace_bytes, void* out, void* stream);
 
 /*
+ * KV write (Spark X2.5-4B F16 vs Q4 comparison, hotelren.com/news/5475707, section 一: 4 KB
+ * of K and V per token and full layer; Sharp-Spark-X2.5-4B-GGUF guide, mpbf.cn/news/67460,
+ * section 三: the sliding layers' cache stays fixed whatever the context, which the
+ * 512-slot ring gives; RoPE of the key as in spark_attn_prefill).
+ *
  * Append `n_new` tokens per sequence to a layer's cache.
  *   k, v   bf16 [batch, n_new, 4, 256], k before RoPE
  *   pos    device int32 [batch]: position of the first new token of each sequence
@@ -202,7 +237,11 @@ size_t spark_attn_decode_workspace_bytes(int32_t layer_type, int32_t batch,
                                          int32_t max_seq_len, int32_t num_parts);
 
 /*
- * Decode: one query token per sequence against the layer's cache.
+ * Decode (Spark X2.5-4B F16 vs Q4 comparison, hotelren.com/news/5475707, section 二: each
+ * generated token re-reads the cached state, so decode is bound by memory bandwidth; the
+ * visible keys, RoPE of the query and the gate as in spark_attn_prefill).
+ *
+ * One query token per sequence against the layer's cache.
  *   q            bf16 [batch, 16, 256], before RoPE; it is rotated at position L-1
  *   gate_logits  bf16 [batch, 16]
  *   cache        the layer's cache, already holding the current token

@@ -30,10 +30,25 @@ def test_exports_every_declared_function():
 
 
 def test_version_and_status_strings():
-    assert fga.abi_version() == 7
+    assert fga.abi_version() == 8
     assert fga.status_string(0) == "ok"
     assert fga.status_string(3) == "workspace too small"
     assert fga.status_string(99) == "unknown status"
+
+
+def test_layer_schedule_from_the_library():
+    """The stack schedule and per-type RoPE come from the C library, and agree with the
+    pages' statement as the oracle writes it down (27 sliding, 9 full, last layer full)."""
+    import oracle
+    types = [fga.layer_type_of(i) for i in range(36)]
+    assert types == [oracle.layer_type_of(i) for i in range(36)]
+    assert types.count(fga.SLIDING) == 27 and types.count(fga.FULL) == 9 and types[35] == fga.FULL
+    assert lib.spark_layer_type_of(-1) == -1 and lib.spark_layer_type_of(36) == -1
+    for lt in (fga.SLIDING, fga.FULL):
+        assert fga.layer_params(lt) == oracle.layer_params(lt)
+    th = ctypes.c_double(-1.0)
+    assert lib.spark_layer_params(2, ctypes.byref(th), None, None) == 1 and th.value == -1.0
+    assert lib.spark_layer_params(0, None, None, None) == 0
 
 
 def _cache(k=FAKE, v=FAKE, batch=1, cap=512):

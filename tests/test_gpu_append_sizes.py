@@ -13,15 +13,6 @@ from test_gpu_q8 import _assert_cache
 pytestmark = pytest.mark.gpu
 
 
-@pytest.fixture(scope="module")
-def fga():
-    import torch
-    if not torch.cuda.is_available():
-        pytest.skip("no GPU")
-    import full_gqa_attention_amd as m
-    return m
-
-
 def _host(t):
     return t.detach().cpu().numpy()
 

@@ -10,15 +10,6 @@ from gpu_util import assert_cached_keys_close, assert_parity, bits_of, f64_of, n
 pytestmark = pytest.mark.gpu
 
 
-@pytest.fixture(scope="module")
-def fga():
-    import torch
-    if not torch.cuda.is_available():
-        pytest.skip("no GPU")
-    import full_gqa_attention_amd as m
-    return m
-
-
 def _capacity(lt, P, n):
     return oracle.WINDOW if lt == oracle.SLIDING else P + n + 3
 

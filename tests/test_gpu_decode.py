@@ -9,15 +9,6 @@ from gpu_util import assert_cached_keys_close, assert_parity, bits_of, f64_of, i
 pytestmark = pytest.mark.gpu
 
 
-@pytest.fixture(scope="module")
-def fga():
-    import torch
-    if not torch.cuda.is_available():
-        pytest.skip("no GPU")
-    import full_gqa_attention_amd as m
-    return m
-
-
 def _ring_from_contiguous(ck, cv, lens):
     """Ring caches holding positions max(0, L-512)..L-1 of contiguous caches, in slot p mod 512."""
     B = ck.shape[0]

@@ -9,15 +9,6 @@ from gpu_util import assert_parity, f64_of, note, to_dev
 pytestmark = pytest.mark.gpu
 
 
-@pytest.fixture(scope="module")
-def fga():
-    import torch
-    if not torch.cuda.is_available():
-        pytest.skip("no GPU")
-    import full_gqa_attention_amd as m
-    return m
-
-
 def _run(fga, inp, lt, cache=None):
     import torch
     q, k, v, g = (to_dev(inp[n]) for n in ("q", "k", "v", "gate"))
@@ -54,14 +45,15 @@ def _sample_rows(S, seed, n_random):
     return np.unique(np.concatenate([fixed, rnd]))
 
 
-def test_full_s8192_sampled_rows(fga):
-    """Single full layer, batch 1, S=8192, theta 5e6 on the first 64 dims: 256 sampled rows."""
+@pytest.mark.timeout(900)
+def test_full_s8192_all_rows(fga):
+    """Single full layer, batch 1, S=8192, theta 5e6 on the first 64 dims: every row."""
     S = 8192
     inp = synth.prefill_inputs(synth.SEED_FULL_S8192, 1, S)
     got = f64_of(_run(fga, inp, oracle.FULL))
-    rows = _sample_rows(S, synth.SEED_FULL_S8192 + 1, 247)
-    want = oracle.prefill(inp["q"], inp["k"], inp["v"], inp["gate"], oracle.FULL, rows=rows)
-    assert_parity(got[:, rows], want, "full S=8192 sampled rows")
+    note("full S=8192: oracle over all 8192 rows")
+    want = oracle.prefill(inp["q"], inp["k"], inp["v"], inp["gate"], oracle.FULL)
+    assert_parity(got, want, "full S=8192 all rows")
 
 
 @pytest.mark.parametrize("layer", list(range(36)))
@@ -100,15 +92,16 @@ def test_prefill_writes_cache(fga, lt, S):
 @pytest.mark.parametrize("lt", [oracle.SLIDING, oracle.FULL], ids=["sliding", "full"])
 def test_prefill_is_deterministic(fga, lt):
     """Repeated calls on the same inputs give bit-identical outputs (no race between the
-    waves of a workgroup or between an MFMA and the instructions that read its result)."""
+    waves of a workgroup or between an MFMA and the instructions that read its result).
+    Every call writes a fresh NaN-filled output through a fresh NaN-filled workspace, so
+    a skipped element cannot pass as an earlier call's result."""
     import torch
     S = 8192
     inp = synth.prefill_inputs(4242 + lt, 1, S)
     q, k, v, g = (to_dev(inp[n]) for n in ("q", "k", "v", "gate"))
-    ws = torch.empty(fga.prefill_workspace_bytes(lt, 1, S), dtype=torch.uint8, device="cuda")
-    ref = fga.prefill(lt, q, k, v, g, workspace=ws).view(torch.int16).clone()
+    ref = fga.prefill(lt, q, k, v, g).view(torch.int16).clone()
     for rep in range(8):
-        out = fga.prefill(lt, q, k, v, g, workspace=ws).view(torch.int16)
+        out = fga.prefill(lt, q, k, v, g).view(torch.int16)
         ndiff = int((out != ref).sum())
         assert ndiff == 0, f"call {rep + 1}: {ndiff} output elements differ from the first call"
 

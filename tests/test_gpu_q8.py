@@ -9,15 +9,6 @@ from gpu_util import assert_parity, f64_of, i32_dev, note, to_dev
 pytestmark = pytest.mark.gpu
 
 
-@pytest.fixture(scope="module")
-def fga():
-    import torch
-    if not torch.cuda.is_available():
-        pytest.skip("no GPU")
-    import full_gqa_attention_amd as m
-    return m
-
-
 def _dev(a):
     import torch
     return torch.from_numpy(np.ascontiguousarray(a)).to("cuda")
@@ -161,6 +152,32 @@ def test_decode_q8_long(fga):
     ring = _ring_of(arrays, lens)
     got = _decode_q8(fga, oracle.SLIDING, q, gate, ring, lens)
     assert_parity(got, oracle.decode_q8(q, gate, *ring, lens, oracle.SLIDING), "decode q8 B=4 L=131072 sliding")
+
+
+@pytest.mark.parametrize("lt", [oracle.SLIDING, oracle.FULL], ids=["sliding", "full"])
+@pytest.mark.parametrize("num_parts", [0, 7, 300])
+def test_decode_q8_is_deterministic(fga, lt, num_parts):
+    """Repeated 8-bit decode calls at batch 64 (lengths uniform in [1024, 32768]) give
+    bit-identical outputs, with the library's partition count and with uneven ones; each
+    call gets a fresh NaN-filled output and workspace.  The K codes pass between the
+    lanes of a wave through LDS, which this would expose if a read overtook a write."""
+    import torch
+    seed = synth.SEED_DECODE_B64 + 11
+    B = 64
+    lens = synth.decode_seq_lens(seed, B, 1024, 32768)
+    cap = 512 if lt == oracle.SLIDING else int(lens.max())
+    arrays = _cache_arrays(seed, B, cap, fill_lens=None if lt == oracle.SLIDING else lens)
+    cache = _gpu_cache(fga, lt, arrays)
+    del arrays
+    q = to_dev(synth.normal_bf16(seed, 0, (B, 16, 256)))
+    g = to_dev(synth.normal_bf16(seed, 1, (B, 16)))
+    L = i32_dev(lens)
+    note(f"decode q8 determinism lt={lt} parts={num_parts}")
+    ref = fga.decode_q8(lt, q, g, cache, L, int(lens.max()), num_parts=num_parts).view(torch.int16).clone()
+    for rep in range(6):
+        out = fga.decode_q8(lt, q, g, cache, L, int(lens.max()), num_parts=num_parts).view(torch.int16)
+        ndiff = int((out != ref).sum())
+        assert ndiff == 0, f"call {rep + 1}: {ndiff} output elements differ from the first call"
 
 
 @pytest.mark.parametrize("lt", [oracle.SLIDING, oracle.FULL], ids=["sliding", "full"])

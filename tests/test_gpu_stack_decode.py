@@ -11,15 +11,6 @@ from gpu_util import assert_parity, f64_of, i32_dev, note, to_dev
 pytestmark = pytest.mark.gpu
 
 
-@pytest.fixture(scope="module")
-def fga():
-    import torch
-    if not torch.cuda.is_available():
-        pytest.skip("no GPU")
-    import full_gqa_attention_amd as m
-    return m
-
-
 def _dev(a):
     import torch
     return torch.from_numpy(np.ascontiguousarray(a)).to("cuda")

@@ -9,15 +9,6 @@ from gpu_util import assert_cached_keys_close, assert_parity, bits_of, f64_of, i
 pytestmark = pytest.mark.gpu
 
 
-@pytest.fixture(scope="module")
-def fga():
-    import torch
-    if not torch.cuda.is_available():
-        pytest.skip("no GPU")
-    import full_gqa_attention_amd as m
-    return m
-
-
 def _packed(seed, lens):
     T = int(sum(lens))
     inp = synth.prefill_inputs(seed, 1, T)
