@@ -426,19 +426,234 @@ __global__ __launch_bounds__(64 * kReduceWaves) void decode_reduce_kernel(Decode
   *reinterpret_cast<u32x2*>(dst) = u32x2{pack_bf16x2(ot[0] * sc, ot[1] * sc), pack_bf16x2(ot[2] * sc, ot[3] * sc)};
 }
 
+// ---------------------------------------------------------------------------------------
+// Sliding layers in one launch.  A sequence sees at most 512 keys, the valid ring slots
+// [0, n) with n = min(L, 512) (softmax does not depend on their order), i.e. at most 16
+// chunks of 32.  Workgroup (b, g) has 8 waves; wave w takes chunks w and w + 8, scoring
+// the 4 query heads of KV head g against their keys with an online softmax.  The 8 states
+// meet in LDS, where the workgroup merges them with log-sum-exp weights and applies the
+// gate: one pass over the ring, no partial results in HBM and no merge launch.  A wave
+// issues its first chunk's K and V loads before anything else and the second chunk's as
+// soon as the first one's registers are consumed (K after the scores, V after the PV
+// sums), so the CU streams its 512 KB share of the ring with about one chunk per wave in
+// flight.
+constexpr int kRingWaves = 8;
+constexpr int kRingChunks = kWindow / kChunk / kRingWaves;   // 2 per wave
+constexpr int kRingVKeys = kChunk / 2;                        // V loads per lane and chunk
+
+// K of keys [ks, ke): lane l takes key ks + 16 kb + l % 16, dims 32 s + 8 (l / 16) .. + 7
+// (the MFMA B operand).  Keys past ke read slot ks (finite, masked by the caller).
+__device__ __forceinline__ void ring_load_k(const DecodeArgs& a, size_t seq_base, int ks, int ke, int lane,
+                                            u32x4 (&kr)[2][8]) {
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    const int key = ks + 16 * kb + (lane & 15);
+    const uint16_t* src = a.cache_k + seq_base + (uint32_t)(key < ke ? key : ks) * kSlot + 8 * (lane >> 4);
+#pragma unroll
+    for (int s = 0; s < 8; ++s) kr[kb][s] = ld_global16(src + 32 * s);
+  }
+}
+
+// V of keys [ks, ke): lane l takes dims 8 (l % 32) .. + 7 of the keys of parity l / 32
+// (two 512-byte rows per load instruction).
+__device__ __forceinline__ void ring_load_v(const DecodeArgs& a, size_t seq_base, int ks, int ke, int lane,
+                                            u32x4 (&vr)[kRingVKeys]) {
+#pragma unroll
+  for (int i = 0; i < kRingVKeys; ++i) {
+    const int key = ks + 2 * i + (lane >> 5);
+    vr[i] = ld_global16(a.cache_v + seq_base + (uint32_t)(key < ke ? key : ks) * kSlot + 8 * (lane & 31));
+  }
+}
+
+__global__ __launch_bounds__(64 * kRingWaves) void decode_ring_kernel(DecodeArgs a) {
+  __shared__ __attribute__((aligned(16))) float s_o[kRingWaves][kGroup][kHeadDim];   // 32 KB
+  __shared__ __attribute__((aligned(16))) float s_p[kRingWaves][kChunk][4];
+  __shared__ float s_ml[kRingWaves][kGroup][2];
+  const int b = blockIdx.x / kKvHeads;
+  const int g = blockIdx.x % kKvHeads;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int L = a.seq_lens[b];
+  const int n = max(0, min(min(L, kWindow), a.cache_cap));
+  const int hrow = lane & 15, kq = lane >> 4;
+  const int vpar = lane >> 5, vdim = 8 * (lane & 31);
+  const size_t seq_base = (size_t)b * a.cache_cap * kSlot + (size_t)g * kHeadDim;
+
+  // The gate logits of the two outputs this thread finishes (heads tid / 256 and + 2 of the
+  // group), Q of the 4 heads of KV head g (lanes 0..15: head l % 16, the first 4 real) and
+  // this wave's first chunk: all loads issued together.
+  const uint16_t g0 = a.gate[(size_t)b * kQHeads + g * kGroup + (tid >> 8)];
+  const uint16_t g1 = a.gate[(size_t)b * kQHeads + g * kGroup + (tid >> 8) + 2];
+  u32x4 raw[8];
+  u32x4 kr[2][8];
+  u32x4 vr[kRingVKeys];
+  const int ks0 = kChunk * w;
+  if (ks0 < n) {
+    if (hrow < kGroup) {
+      const uint16_t* qrow = a.q + ((size_t)b * kQHeads + g * kGroup + hrow) * kHeadDim;
+#pragma unroll
+      for (int s = 0; s < 8; ++s) raw[s] = ld_global16(qrow + 32 * s + 8 * kq);
+    } else {
+#pragma unroll
+      for (int s = 0; s < 8; ++s) raw[s] = u32x4{0, 0, 0, 0};
+    }
+    ring_load_k(a, seq_base, ks0, min(ks0 + kChunk, n), lane, kr);
+    ring_load_v(a, seq_base, ks0, min(ks0 + kChunk, n), lane, vr);
+  }
+
+  float m_run[4], l_run[4], acc[4][8];
+#pragma unroll
+  for (int h = 0; h < 4; ++h) {
+    m_run[h] = -1e30f;
+    l_run[h] = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[h][e] = 0.0f;
+  }
+  if (ks0 < n) {
+    // Q rotated at position L - 1 (frequencies from the compile-time table) while the K and
+    // V loads are in flight.
+    bf16x8 qa[8];
+    if (hrow < kGroup) {
+      // Pair 32 s + 8 kq + j: the table entry of 32 s + j (a constant) times theta^(-16 kq / r).
+      const double f = kq == 0 ? kRopeStep8[0] : kq == 1 ? kRopeStep8[1] : kq == 2 ? kRopeStep8[2] : kRopeStep8[3];
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        rope_rotate_pairs(raw[s], raw[s + 4], (double)(L - 1),
+                          [&](int j) { return kRopeSliding.inv_rev[32 * s + j] * f; });
+    }
+#pragma unroll
+    for (int s = 0; s < 8; ++s) qa[s] = as_bf16x8(raw[s]);
+    // One chunk [ks, ke) on the K and V now in registers; after_scores() runs once the K
+    // registers are consumed, after_pv() once the V registers are.
+    auto chunk = [&](int ks, int ke, auto after_scores, auto after_pv) {
+      // Scores: lanes 0..15 hold heads 0..3 (element v) for key ks + 16 kb + lane.
+      float t[2][4];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        f32x4 sc = f32x4{0, 0, 0, 0};
+#pragma unroll
+        for (int s = 0; s < 8; ++s) sc = mfma_16x16x32(qa[s], as_bf16x8(kr[kb][s]), sc);
+        const bool ok = ks + 16 * kb + hrow < ke;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) t[kb][v] = ok ? sc[v] * kScoreScaleLog2 : -INFINITY;
+      }
+      after_scores();
+      float alpha[4];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        float mx = fmaxf(t[0][v], t[1][v]);
+#pragma unroll
+        for (int off = 1; off < 16; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+        const float m_new = fmaxf(m_run[v], mx);
+        alpha[v] = __builtin_amdgcn_exp2f(m_run[v] - m_new);
+        const float p0 = __builtin_amdgcn_exp2f(t[0][v] - m_new);
+        const float p1 = __builtin_amdgcn_exp2f(t[1][v] - m_new);
+        t[0][v] = p0;
+        t[1][v] = p1;
+        float ps = p0 + p1;
+#pragma unroll
+        for (int off = 1; off < 16; off <<= 1) ps += __shfl_xor(ps, off);
+        l_run[v] = l_run[v] * alpha[v] + ps;
+        m_run[v] = m_new;
+        // Lanes 16..63 reduced the padding rows of the MFMA, not these heads: every lane
+        // rescales its value sums by lane 0's factor.
+        alpha[v] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha[v]), 0));
+      }
+      // P through this wave's own LDS rows to the lanes that own the value dims.  One wave
+      // issues its LDS operations in order, so the wave barriers (which only keep the
+      // compiler from moving the accesses across them) suffice between its writes and reads.
+      if (lane < 16) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+          *reinterpret_cast<f32x4*>(&s_p[w][16 * kb + lane][0]) = f32x4{t[kb][0], t[kb][1], t[kb][2], t[kb][3]};
+      }
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int h = 0; h < 4; ++h)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[h][e] *= alpha[h];
+#pragma unroll
+      for (int i = 0; i < kRingVKeys; ++i) {
+        const f32x4 pp = *reinterpret_cast<const f32x4*>(&s_p[w][2 * i + vpar][0]);
+        float x[8];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          x[2 * q] = bf16_lo(vr[i][q]);
+          x[2 * q + 1] = bf16_hi(vr[i][q]);
+        }
+#pragma unroll
+        for (int h = 0; h < 4; ++h)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[h][e] += pp[h] * x[e];
+      }
+      __builtin_amdgcn_wave_barrier();
+      after_pv();
+    };
+    static_assert(kRingChunks == 2, "two chunks per wave");
+    // The second chunk's loads are unconditional (no register of the first chunk has to
+    // survive them): when it lies past n its rows are clamped into the 512-slot ring and
+    // never used.
+    const int ks1 = ks0 + kChunk * kRingWaves;
+    const int ke1 = max(min(ks1 + kChunk, n), ks1);
+    chunk(ks0, min(ks0 + kChunk, n),
+          [&] {
+            __builtin_amdgcn_sched_barrier(0);   // not hoisted above the scores (registers)
+            ring_load_k(a, seq_base, ks1, ke1, lane, kr);
+          },
+          [&] {
+            __builtin_amdgcn_sched_barrier(0);   // not hoisted above the PV sums (registers)
+            ring_load_v(a, seq_base, ks1, ke1, lane, vr);
+          });
+    if (ks1 < n) chunk(ks1, ke1, [] {}, [] {});
+    // Lanes holding the same dims of the other key parity.
+#pragma unroll
+    for (int h = 0; h < 4; ++h)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[h][e] += __shfl_xor(acc[h][e], 32);
+  }
+  // Every wave's state into LDS (a wave without keys: m = -1e30, l = 0, O = 0).
+  if (lane < 32) {
+#pragma unroll
+    for (int h = 0; h < 4; ++h)
+#pragma unroll
+      for (int e = 0; e < 8; e += 4)
+        *reinterpret_cast<f32x4*>(&s_o[w][h][vdim + e]) = f32x4{acc[h][e], acc[h][e + 1], acc[h][e + 2], acc[h][e + 3]};
+  }
+  if (lane < 4) {
+    s_ml[w][lane][0] = m_run[lane];
+    s_ml[w][lane][1] = l_run[lane];
+  }
+  __syncthreads();
+  // Thread t merges head h = idx / 256 of the group, dim d = idx % 256, idx = t and t + 512.
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int idx = tid + 64 * kRingWaves * j;
+    const int h = idx >> 8, d = idx & 255;
+    float M = -1e30f;
+#pragma unroll
+    for (int v = 0; v < kRingWaves; ++v) M = fmaxf(M, s_ml[v][h][0]);
+    float lsum = 0.0f, o = 0.0f;
+#pragma unroll
+    for (int v = 0; v < kRingWaves; ++v) {
+      const float sv = __builtin_amdgcn_exp2f(s_ml[v][h][0] - M);
+      lsum += s_ml[v][h][1] * sv;
+      o += s_o[v][h][d] * sv;
+    }
+    const int hq = g * kGroup + h;
+    const float gl = bf16_to_f32(j == 0 ? g0 : g1);
+    const float scale = lsum > 0.0f ? sigmoidf_fast(gl) / lsum : 0.0f;   // no visible key: zeros
+    a.out[((size_t)b * kQHeads + hq) * kHeadDim + d] = (uint16_t)(pack_bf16x2(o * scale, 0.0f) & 0xffffu);
+  }
+}
+
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// Partitions chosen automatically (bf16 cache): one per CU of the current device.  On MI355X (256 CUs)
-// one 4-wave workgroup per CU streams faster than two or more: fewer concurrent streams,
-// each reading 64 KB of consecutive K (and V) slots per step, keep HBM rows open longer,
-// and each extra partition adds a 16 KB partial result to write and merge.
-int cu_count() {
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
-    cus = 256;
-  return cus;
-}
+// Partitions chosen automatically (bf16 cache): one per CU of MI355X (256 CUs).  One 4-wave
+// workgroup per CU streams faster than two or more: fewer concurrent streams, each reading
+// 64 KB of consecutive K (and V) slots per step, keep HBM rows open longer, and each extra
+// partition adds a 16 KB partial result to write and merge.  A constant, not a query of the
+// current device, so that the workspace size depends on the call's arguments alone.
+constexpr int kDefaultParts = 256;
 
 }  // namespace
 
@@ -452,7 +667,7 @@ DecodePlan plan_decode(int layer_type, int batch, int max_seq_len, int nparts, b
   const long long max_chunks = (long long)batch * ((n + kChunk - 1) / kChunk);
   int P = nparts;
   if (P <= 0) {
-    const int want = (q8 ? 2 : 1) * cu_count();
+    const int want = (q8 ? 2 : 1) * kDefaultParts;
     P = (int)(max_chunks < want ? max_chunks : want);
     if (P < 1) P = 1;
   }
@@ -465,14 +680,27 @@ DecodePlan plan_decode(int layer_type, int batch, int max_seq_len, int nparts, b
   return p;
 }
 
+// bf16 sliding layers of a batch of at least 16 sequences: the one-launch ring kernel.
+// Smaller batches give it too few workgroups (4 per sequence) to hide its three dependent
+// memory round trips (Q with the first chunk, the second chunk's K, then its V): at batch 1
+// and 4 it took 21 us against 16 us for split + merge, at batch 64 27 us against 32 us.
+// Everything else runs split + merge (the 8-bit variant of the ring kernel ran out of
+// registers with two chunks per wave: 93 spilled VGPRs).
+constexpr int kRingMinBatch = 16;
+
 template <bool Q8>
 hipError_t launch_decode_impl(int layer_type, const DecodeArgs& a, hipStream_t stream) {
-  const dim3 grid_reduce(a.batch * kQHeads);
+  if constexpr (!Q8) {
+    if (layer_type == kSliding && a.batch >= kRingMinBatch) {
+      hipLaunchKernelGGL(decode_ring_kernel, dim3(a.batch * kKvHeads), dim3(64 * kRingWaves), 0, stream, a);
+      return hipGetLastError();
+    }
+  }
   if (layer_type == kSliding)
     hipLaunchKernelGGL((decode_split_kernel<kSliding, Q8>), dim3(a.nparts), dim3(kThreads), 0, stream, a);
   else
     hipLaunchKernelGGL((decode_split_kernel<kFull, Q8>), dim3(a.nparts), dim3(kThreads), 0, stream, a);
-  hipLaunchKernelGGL(decode_reduce_kernel, grid_reduce, dim3(64 * kReduceWaves), 0, stream, a);
+  hipLaunchKernelGGL(decode_reduce_kernel, dim3(a.batch * kQHeads), dim3(64 * kReduceWaves), 0, stream, a);
   return hipGetLastError();
 }
 

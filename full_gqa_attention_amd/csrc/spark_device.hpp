@@ -82,6 +82,54 @@ __device__ __forceinline__ double rope_inv_rev(int m, int rot, double log2_theta
   return exp2(-(2.0 * m / rot) * log2_theta) * 0.15915494309189535;
 }
 
+// The same inverse frequencies as a table evaluated at compile time, for kernels that
+// should not spend a barrier and an fp64 exp2 per workgroup on them: natural log by the
+// atanh series after reducing to [1, 2), exp2 by the Taylor series of e^y after splitting
+// off the integer part.  Relative error below 3e-15 (the fp64 rounding of log2 theta,
+// scaled by the exponent), i.e. under 1e-9 revolution of angle at position 2^20.
+namespace cx {
+constexpr double kLn2 = 0.69314718055994530942;
+constexpr double ln(double x) {
+  int k = 0;
+  while (x >= 2.0) { x *= 0.5; ++k; }
+  while (x < 1.0) { x *= 2.0; --k; }
+  const double z = (x - 1.0) / (x + 1.0), z2 = z * z;
+  double term = z, sum = 0.0;
+  for (int i = 0; i < 60; ++i) { sum += term / (2 * i + 1); term *= z2; }
+  return 2.0 * sum + k * kLn2;
+}
+constexpr double exp2(double x) {
+  int n = 0;
+  while (x > 0.5) { x -= 1.0; ++n; }
+  while (x < -0.5) { x += 1.0; --n; }
+  const double y = x * kLn2;
+  double term = 1.0, sum = 1.0;
+  for (int i = 1; i < 30; ++i) { term *= y / i; sum += term; }
+  for (; n > 0; --n) sum *= 2.0;
+  for (; n < 0; ++n) sum *= 0.5;
+  return sum;
+}
+}  // namespace cx
+
+template <int LT>
+struct RopeTable {
+  double inv_rev[LayerTraits<LT>::kRot / 2];   // theta^(-2m/r) / (2 pi), revolutions per position
+};
+template <int LT>
+constexpr RopeTable<LT> make_rope_table() {
+  using T = LayerTraits<LT>;
+  RopeTable<LT> t{};
+  const double log2_theta = cx::ln(T::kTheta) / cx::kLn2;
+  for (int m = 0; m < T::kRot / 2; ++m) t.inv_rev[m] = cx::exp2(-(2.0 * m / T::kRot) * log2_theta) * 0.15915494309189535;
+  return t;
+}
+constexpr RopeTable<kSliding> kRopeSliding = make_rope_table<kSliding>();
+// theta^(-2 d / r) of the sliding layer for a pair offset d = 8 k, k = 0..3.
+constexpr double rope_step8(int k) {
+  return cx::exp2(-(2.0 * 8 * k / LayerTraits<kSliding>::kRot) * (cx::ln(LayerTraits<kSliding>::kTheta) / cx::kLn2));
+}
+constexpr double kRopeStep8[4] = {1.0, rope_step8(1), rope_step8(2), rope_step8(3)};
+
 // cos and sin of the rotary angle of position p for a pair whose inverse frequency is
 // inv_rev revolutions per position.  The angle is reduced to [0, 1) revolution in fp64
 // (exact to ~1e-10 rev for p < 2^20) before the hardware sin/cos, whose argument is in
@@ -94,16 +142,16 @@ __device__ __forceinline__ void rope_cos_sin(double p, double inv_rev, float& c,
   c = __builtin_amdgcn_cosf(f);
 }
 
-// Rotate the 8 pairs (x1[j], x2[j]) held as two 16-byte bf16 chunks, in place, with
-// inverse frequencies inv[m0 + j] at position p.
-__device__ __forceinline__ void rope_rotate_chunks(u32x4& x1, u32x4& x2, double p,
-                                                   const double* inv, int m0) {
+// Rotate the 8 pairs (x1[j], x2[j]) held as two 16-byte bf16 chunks, in place, at
+// position p; inv(j) gives pair j's inverse frequency in revolutions per position.
+template <class Inv>
+__device__ __forceinline__ void rope_rotate_pairs(u32x4& x1, u32x4& x2, double p, Inv inv) {
   u32x4 y1, y2;
 #pragma unroll
   for (int w = 0; w < 4; ++w) {
     float c0, s0, c1, s1;
-    rope_cos_sin(p, inv[m0 + 2 * w], c0, s0);
-    rope_cos_sin(p, inv[m0 + 2 * w + 1], c1, s1);
+    rope_cos_sin(p, inv(2 * w), c0, s0);
+    rope_cos_sin(p, inv(2 * w + 1), c1, s1);
     const float a0 = bf16_lo(x1[w]), a1 = bf16_hi(x1[w]);
     const float b0 = bf16_lo(x2[w]), b1 = bf16_hi(x2[w]);
     y1[w] = pack_bf16x2(a0 * c0 - b0 * s0, a1 * c1 - b1 * s1);
@@ -114,6 +162,12 @@ __device__ __forceinline__ void rope_rotate_chunks(u32x4& x1, u32x4& x2, double 
   }
   x1 = y1;
   x2 = y2;
+}
+
+// The same with inverse frequencies inv[m0 + j] (a table in LDS).
+__device__ __forceinline__ void rope_rotate_chunks(u32x4& x1, u32x4& x2, double p,
+                                                   const double* inv, int m0) {
+  rope_rotate_pairs(x1, x2, p, [&](int j) { return inv[m0 + j]; });
 }
 
 __device__ __forceinline__ float sigmoidf_fast(float g) {

@@ -110,7 +110,7 @@ def test_workspace_planning():
     assert ws(1, 1, 64, 2) == _layout_bytes(1, 2)
     assert ws(1, 3, 64, 5000) == _layout_bytes(3, 5000)
     # Library's choice: never more partitions than 32-key chunks in the batch, at most one
-    # per CU (256 on MI355X; the CPU test host has no device, so it plans for 256).
+    # per CU of MI355X (256, a constant: the size never depends on the current device).
     assert ws(1, 1, 64) == _layout_bytes(1, 2)
     assert ws(0, 1, 100000) == _layout_bytes(1, 16)       # ring: <= 512 keys = 16 chunks
     assert ws(1, 64, 32768) == _layout_bytes(64, 256)

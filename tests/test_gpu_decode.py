@@ -193,6 +193,43 @@ def test_decode_batch_beyond_plan_threads(fga, num_parts):
     assert np.all(got[~live] == 0.0)
 
 
+RING_LENS = [0, 1, 5, 31, 32, 33, 255, 256, 257, 480, 511, 512, 513, 700, 1000, 2049, 17, 300, 64, 96]
+
+
+def test_sliding_ring_batch_edges(fga):
+    """A batch of 20 on a sliding layer (the one-launch ring kernel, used from batch 16 on):
+    an empty sequence, ragged chunks, waves whose second chunk is empty, partly filled and
+    full, and rings holding more positions than the window."""
+    lens = np.array(RING_LENS, np.int32)
+    B = len(lens)
+    d = synth.decode_inputs(4400, B, int(lens.max()), fill_lens=lens)
+    rk, rv = _ring_from_contiguous(d["cache_k"], d["cache_v"], lens)
+    got = _decode_dev(fga, oracle.SLIDING, d, rk, rv, lens)
+    live = lens > 0
+    assert np.all(got[~live] == 0.0)
+    want = oracle.decode(d["q"][live], d["gate"][live], rk[live], rv[live], lens[live], oracle.SLIDING)
+    assert_parity(got[live], want, "decode sliding ring, batch 20 of edge lengths")
+
+
+def test_sliding_ring_is_deterministic(fga):
+    """Repeated ring-kernel calls at batch 64 give bit-identical outputs (fresh NaN-filled
+    outputs each call): the 8 waves' states meet in LDS behind one barrier."""
+    import torch
+    B = 64
+    lens = synth.decode_seq_lens(4500, B, 1024, 32768)
+    rk = synth.normal_bf16(4500, 0, (B, 512, 4, 256))
+    rv = synth.normal_bf16(4500, 1, (B, 512, 4, 256))
+    cache = fga.KVCache(oracle.SLIDING, B, 512, k=to_dev(rk), v=to_dev(rv))
+    q = to_dev(synth.normal_bf16(4500, 2, (B, 16, 256)))
+    g = to_dev(synth.normal_bf16(4500, 3, (B, 16)))
+    L = i32_dev(lens)
+    ref = fga.decode(oracle.SLIDING, q, g, cache, L, int(lens.max())).view(torch.int16).clone()
+    for rep in range(8):
+        out = fga.decode(oracle.SLIDING, q, g, cache, L, int(lens.max())).view(torch.int16)
+        ndiff = int((out != ref).sum())
+        assert ndiff == 0, f"call {rep + 1}: {ndiff} output elements differ from the first call"
+
+
 def test_decode_is_deterministic(fga):
     """Repeated decode calls on the same cache give bit-identical outputs."""
     import torch
