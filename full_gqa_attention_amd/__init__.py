@@ -70,6 +70,8 @@ def _load():
     lib.spark_attn_decode_workspace_bytes.restype = sz
     lib.spark_attn_decode.argtypes = [i32, i32, vp, vp, cache_p, vp, i32, i32, vp, sz, vp, vp]
     lib.spark_attn_decode.restype = i32
+    lib.spark_attn_decode_noalloc.argtypes = [i32, i32, vp, vp, cache_p, vp, i32, i32, vp, vp]
+    lib.spark_attn_decode_noalloc.restype = i32
     q8_p = ctypes.POINTER(KvCacheQ8Desc)
     lib.spark_kv_append_q8.argtypes = [i32, i32, i32, vp, vp, vp, q8_p, vp]
     lib.spark_kv_append_q8.restype = i32
@@ -96,7 +98,7 @@ EXPORTED = ("spark_attn_prefill_workspace_bytes", "spark_attn_prefill", "spark_a
             "spark_attn_prefill_varlen", "spark_qkv_proj_fp8_workspace_bytes", "spark_qkv_proj_fp8",
             "spark_kv_append", "spark_attn_decode_workspace_bytes",
             "spark_attn_decode", "spark_kv_append_q8", "spark_attn_decode_q8_workspace_bytes", "spark_attn_decode_q8", "spark_status_string",
-            "spark_abi_version", "spark_layer_type_of", "spark_layer_params")
+            "spark_abi_version", "spark_layer_type_of", "spark_layer_params", "spark_attn_decode_noalloc")
 
 
 def abi_version() -> int:
@@ -343,6 +345,31 @@ def decode(layer_type: int, q, gate, cache: KVCache, seq_lens, max_seq_len: int,
                                 int(workspace.numel()), _ptr(out), _stream(stream))
     if st:
         raise SparkError(st, "spark_attn_decode")
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 16 << 20
+
+
+def decode_noalloc(layer_type: int, q, gate, cache: KVCache, seq_lens, max_seq_len: int, out=None,
+                   num_parts: int = 0, stream=None):
+    """spark_attn_decode_noalloc: decode with the library's static device scratch instead of
+    a workspace; arguments as for decode.  Calls that may overlap on one GPU race."""
+    torch = _torch()
+    B = int(q.shape[0])
+    _check(q, "q", (B, N_Q_HEADS, HEAD_DIM), torch.bfloat16)
+    _check(gate, "gate", (B, N_Q_HEADS), torch.bfloat16)
+    _check(seq_lens, "seq_lens", (B,), torch.int32)
+    if cache.layer_type != layer_type:
+        raise ValueError("cache layer type differs from the call's")
+    if out is None:
+        out = torch.empty_like(q)
+    _check(out, "out", tuple(q.shape), torch.bfloat16)
+    st = _lib.spark_attn_decode_noalloc(int(layer_type), B, _ptr(q), _ptr(gate), ctypes.pointer(cache.desc()),
+                                        _ptr(seq_lens), int(max_seq_len), int(num_parts), _ptr(out),
+                                        _stream(stream))
+    if st:
+        raise SparkError(st, "spark_attn_decode_noalloc")
     return out
 
 

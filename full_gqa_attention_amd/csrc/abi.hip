@@ -39,17 +39,26 @@ size_t varlen_queue_offset(int32_t total_tokens) {
   return (spark::prefill_workspace_bytes(1, total_tokens) + 255) & ~(size_t)255;
 }
 
-// Checks shared by spark_attn_decode and spark_attn_decode_q8 (everything but the cache).
-spark_status check_decode(int32_t layer_type, int32_t batch, const void* q, const void* gate_logits,
-                          const int32_t* seq_lens, int32_t max_seq_len, int32_t num_parts,
-                          const void* workspace, const void* out) {
+// Checks shared by the decode entry points (everything but the cache and the workspace).
+spark_status check_decode_io(int32_t layer_type, int32_t batch, const void* q, const void* gate_logits,
+                             const int32_t* seq_lens, int32_t max_seq_len, int32_t num_parts,
+                             const void* out) {
   if (!valid_type(layer_type)) return SPARK_ERR_INVALID_ARG;
   if (batch < 1 || batch > kMaxBatch || max_seq_len < 1 || max_seq_len > kMaxSeq) return SPARK_ERR_INVALID_ARG;
   if (num_parts < 0 || num_parts > kMaxParts) return SPARK_ERR_INVALID_ARG;
-  if (!q || !gate_logits || !seq_lens || !out || !workspace) return SPARK_ERR_INVALID_ARG;
-  if (!aligned16(q) || !aligned16(out) || !aligned2(gate_logits) ||
-      (reinterpret_cast<uintptr_t>(seq_lens) & 3u) || (reinterpret_cast<uintptr_t>(workspace) & 255u))
+  if (!q || !gate_logits || !seq_lens || !out) return SPARK_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(out) || !aligned2(gate_logits) || (reinterpret_cast<uintptr_t>(seq_lens) & 3u))
     return SPARK_ERR_INVALID_ARG;
+  return SPARK_OK;
+}
+
+// ... and the caller's workspace of spark_attn_decode and spark_attn_decode_q8.
+spark_status check_decode(int32_t layer_type, int32_t batch, const void* q, const void* gate_logits,
+                          const int32_t* seq_lens, int32_t max_seq_len, int32_t num_parts,
+                          const void* workspace, const void* out) {
+  const spark_status st = check_decode_io(layer_type, batch, q, gate_logits, seq_lens, max_seq_len, num_parts, out);
+  if (st != SPARK_OK) return st;
+  if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u)) return SPARK_ERR_INVALID_ARG;
   return SPARK_OK;
 }
 
@@ -280,6 +289,25 @@ spark_status spark_attn_decode(int32_t layer_type, int32_t batch, const void* q,
   const spark::DecodePlan plan = spark::plan_decode(layer_type, batch, max_seq_len, num_parts);
   if (workspace_bytes < plan.total_bytes) return SPARK_ERR_WORKSPACE;
   spark::DecodeArgs a = decode_args(plan, batch, cache->capacity, q, gate_logits, seq_lens, workspace, out);
+  a.cache_k = static_cast<const uint16_t*>(cache->k);
+  a.cache_v = static_cast<const uint16_t*>(cache->v);
+  return from_hip(spark::launch_decode(layer_type, a, static_cast<hipStream_t>(stream)));
+}
+
+spark_status spark_attn_decode_noalloc(int32_t layer_type, int32_t batch, const void* q,
+                                       const void* gate_logits, const spark_kv_cache* cache,
+                                       const int32_t* seq_lens, int32_t max_seq_len,
+                                       int32_t num_parts, void* out, void* stream) {
+  spark_status st = check_decode_io(layer_type, batch, q, gate_logits, seq_lens, max_seq_len, num_parts, out);
+  if (st != SPARK_OK) return st;
+  st = check_cache(layer_type, cache, batch);
+  if (st != SPARK_OK) return st;
+  if (layer_type == SPARK_LAYER_FULL && max_seq_len > cache->capacity) return SPARK_ERR_INVALID_ARG;
+  const spark::DecodePlan plan = spark::plan_decode(layer_type, batch, max_seq_len, num_parts);
+  if (plan.total_bytes > spark::kStaticScratchBytes) return SPARK_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if (spark::static_scratch(&ws) != hipSuccess) return SPARK_ERR_HIP;
+  spark::DecodeArgs a = decode_args(plan, batch, cache->capacity, q, gate_logits, seq_lens, ws, out);
   a.cache_k = static_cast<const uint16_t*>(cache->k);
   a.cache_v = static_cast<const uint16_t*>(cache->v);
   return from_hip(spark::launch_decode(layer_type, a, static_cast<hipStream_t>(stream)));

@@ -108,4 +108,9 @@ struct DecodePlan {
 };
 DecodePlan plan_decode(int layer_type, int batch, int max_seq_len, int nparts, bool q8 = false);
 
+// Static device scratch of spark_attn_decode_noalloc: its size, and its device address on
+// the current device (looked up on the first call per device).
+constexpr size_t kStaticScratchBytes = (size_t)16 << 20;
+hipError_t static_scratch(void** ptr);
+
 }  // namespace spark

@@ -268,6 +268,28 @@ spark_status spark_attn_decode(int32_t layer_type, int32_t batch, const void* q,
                                size_t workspace_bytes, void* out, void* stream);
 
 /*
+ * spark_attn_decode for callers that cannot allocate device memory (code under HIP graph
+ * capture, serving loops and harnesses that forbid hipMalloc): no workspace argument.  The
+ * partial results live in a static device array of SPARK_DECODE_NOALLOC_SCRATCH_BYTES
+ * (16 MiB) that the library holds on every GPU it runs on until the process ends; the call
+ * itself allocates and frees nothing.  Its first call on a device, with that device
+ * current, looks the array's device address up (hipGetSymbolAddress; a failure returns
+ * SPARK_ERR_HIP).  Arguments, limits and results are those of spark_attn_decode; a shape
+ * whose spark_attn_decode_workspace_bytes(layer_type, batch, max_seq_len, num_parts)
+ * exceeds the array returns SPARK_ERR_WORKSPACE with nothing enqueued (batch 64 with the
+ * library's partition count needs about 5 MiB).  Nothing
+ * in the array has to start at zero: each call writes every byte it reads before reading
+ * it.  All calls on one GPU share the array, which keeps the last call's contents, so
+ * calls that may overlap on one GPU (other streams, or other host threads without an
+ * order between their streams) race and give undefined results.
+ */
+#define SPARK_DECODE_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+spark_status spark_attn_decode_noalloc(int32_t layer_type, int32_t batch, const void* q,
+                                       const void* gate_logits, const spark_kv_cache* cache,
+                                       const int32_t* seq_lens, int32_t max_seq_len,
+                                       int32_t num_parts, void* out, void* stream);
+
+/*
  * 8-bit KV cache of one layer: the q8_0 format the Sharp-Spark-X2.5-4B-GGUF guide
  * (mpbf.cn/news/67460, section 四) enables with --cache-type-k/v q8_0, 36 -> 19 KB per
  * token over the 9 full layers.  Each K or V row of 256 values is 8 blocks of 32; a block

@@ -129,6 +129,20 @@ def test_decode_rejects():
     assert f(0, 1, FAKE, FAKE, _cache(cap=1024), FAKE, 64, 0, FAKE, big, FAKE, None) == 1
 
 
+def test_decode_noalloc_rejects():
+    """Checks of the entry point without a workspace, all before any HIP call."""
+    f = lib.spark_attn_decode_noalloc
+    assert f(1, 1, FAKE, FAKE, _cache(cap=64), FAKE, 65, 0, FAKE, None) == 1      # > capacity
+    assert f(1, 1, FAKE, FAKE, _cache(cap=64), FAKE, 64, -1, FAKE, None) == 1     # parts < 0
+    assert f(1, 1, None, FAKE, _cache(cap=64), FAKE, 64, 0, FAKE, None) == 1      # no q
+    assert f(1, 1, FAKE, FAKE, _cache(cap=64), FAKE, 64, 0, MISALIGNED, None) == 1
+    assert f(0, 1, FAKE, FAKE, _cache(cap=1024), FAKE, 64, 0, FAKE, None) == 1    # ring != 512
+    # Beyond the 16 MiB static scratch: 256 + 1000 partial results, or 4000 + 1.
+    assert fga.decode_workspace_bytes(1, 1000, 64) > fga.NOALLOC_SCRATCH_BYTES
+    assert f(1, 1000, FAKE, FAKE, _cache(batch=1000, cap=64), FAKE, 64, 0, FAKE, None) == 3
+    assert f(1, 1, FAKE, FAKE, _cache(cap=64), FAKE, 64, 4000, FAKE, None) == 3
+
+
 def _cache_q8(k=FAKE, ks=FAKE, v=FAKE, vs=FAKE, batch=1, cap=512):
     val = lambda p: p.value if p else None
     return ctypes.pointer(fga.KvCacheQ8Desc(val(k), val(ks), val(v), val(vs), batch, cap))
