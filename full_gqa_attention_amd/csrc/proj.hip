@@ -98,11 +98,15 @@ __global__ __launch_bounds__(256) void quant_gate_kernel(ProjArgs a) {
 // FP8 GEMM.  Workgroup tiles of tokens x channels on WM x WN waves, each wave owning
 // BMW x BNW blocks of 32 x 32; K in stages of BK bytes (64 or 128) through a ring of S LDS
 // stages, each filled S - 1 stages ahead.  In a stage, operand row r holds its BK / 16
-// chunks of 16 bytes at r BK + 16 (c ^ swz(r)) with swz(r) = r & 7 (BK = 128) or
-// (r / 4) & 3 (BK = 64): the rows one read instruction's lane groups touch then hit
-// distinct banks.  A direct load fills one kilobyte (1024 / BK rows) per instruction: lane
-// l writes bytes 16 l .. 16 l + 15 of the block, i.e. row l / (BK / 16) and physical chunk
-// l % (BK / 16), so it fetches the logical chunk whose swizzled place that is.
+// chunks of 16 bytes at r BK + 16 (c ^ swz(r)) with swz(r) = (r / 2) & 7 (BK = 128) or
+// (r / 4) & 3 (BK = 64).  LDS serves a 16-byte read 16 lanes at a time over 64 banks
+// (256 bytes): the 16 rows such a group reads (one chunk each) then land on 16 distinct
+// 16-byte bank groups, 256 / BK rows per bank row times 16 / (256 / BK) swizzle values.
+// (With swz(r) = r & 7 at BK = 128, rows r and r + 8 met in one bank group: the counters
+// showed half of all LDS cycles as bank conflicts.)  A direct load fills one kilobyte
+// (1024 / BK rows) per instruction: lane l writes bytes 16 l .. 16 l + 15 of the block,
+// i.e. row l / (BK / 16) of the block and physical chunk l % (BK / 16), so it fetches
+// the logical chunk whose swizzled place that is.
 
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"   // M0 in the clobber list: nothing else uses it
@@ -126,7 +130,7 @@ __device__ __forceinline__ void wait_vmcnt() {                // vmcnt <= N, oth
 }
 
 template <int BK>
-__device__ __forceinline__ int swz(int r) { return BK == 128 ? (r & 7) : ((r >> 2) & 3); }
+__device__ __forceinline__ int swz(int r) { return BK == 128 ? ((r >> 1) & 7) : ((r >> 2) & 3); }
 
 // Row r, logical 16-byte chunk c of a stage buffer.
 template <int BK>
@@ -167,11 +171,12 @@ __global__ __launch_bounds__(64 * WM * WN) void qkv_gemm_kernel(ProjArgs a) {
   // wave + kWaves (i - kXLoads): which operand is known at compile time.  Per-lane byte
   // offsets from the operand's base (token rows past the end read the last row; their
   // results are not stored).
-  const int lr = lane / G::kChunks, lc = (lane % G::kChunks) ^ swz<BK>(lr);
+  const int lr = lane / G::kChunks;
   uint32_t off[G::kLoads];
 #pragma unroll
   for (int i = 0; i < G::kLoads; ++i) {
     const int blk = wave + G::kWaves * (i < G::kXLoads ? i : i - G::kXLoads);
+    const int lc = (lane % G::kChunks) ^ swz<BK>(G::kBlockRows * blk + lr);   // stage row of this lane
     off[i] = i < G::kXLoads ? (uint32_t)min(m0 + G::kBlockRows * blk + lr, T - 1) * kHidden + 16 * lc
                             : (uint32_t)(n0 + G::kBlockRows * blk + lr) * kHidden + 16 * lc;
   }
