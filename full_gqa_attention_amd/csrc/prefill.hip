@@ -618,6 +618,209 @@ void prefill_kernel(PrefillArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------------------
+// Sliding layers of short sequences, whose 64-row query blocks cannot fill the chip (at
+// S = 1024: 16 blocks x 4 KV heads = 64 workgroups for 256 CUs, each walking up to 18
+// dependent tiles).  Here a workgroup takes 32 query positions of one (sequence, KV head)
+// and its 8 waves are the 4 query heads times the two halves of the key band: wave w
+// computes head 4g + w % 4 over the tiles of half w / 4, so the dependent chain is at most
+// 9 tiles and twice as many workgroups run.  Each half streams its tiles through its own
+// two-stage ring (prefetch one tile ahead); at the end the second half's (max, sum, O) go
+// through LDS to the wave of the same head in the first half, which merges them with
+// log-sum-exp weights and runs the usual gated epilogue.
+
+constexpr int kSplitRows = 32;                       // query positions per workgroup
+constexpr int kSplitLoads = 2 * (kKLoads + kVLoads);   // load instructions per wave and tile
+
+// One tile (keys k0 .. k0 + 31, K in ks, V in vs) for the 32 rows starting at position r0,
+// lane row r32: S^T = K Q^T, band mask on edge tiles, lazy online softmax, O^T += V^T P^T.
+// The same arithmetic as a step of prefill_kernel (whose prefetches are interleaved).
+__device__ __forceinline__ void split_tile(const uint8_t* ks, const uint8_t* vs, int k0, int r0, int lane,
+                                           const bf16x8 (&qf)[16], f32x16 (&o)[8], float& m_run, float& l_part,
+                                           int v_lane_off) {
+  const int half = lane >> 5, r32 = lane & 31;
+  const int vr = (lane >> 2) & 3;
+  const bool any = (k0 <= r0 + 31) && (k0 + kBN - 1 >= r0 - (kWindow - 1));
+  if (!any) return;                                  // wave-uniform: no row of the block sees the tile
+  const bool edge = (k0 + kBN - 1 > r0) || (k0 < r0 + 31 - (kWindow - 1));
+  f32x16 sacc = f32x16{0};
+#pragma unroll
+  for (int s = 0; s < 16; ++s) {
+    const bf16x8 ka = as_bf16x8(*reinterpret_cast<const u32x4*>(ks + (32 * (2 * s + half) + r32) * 16));
+    sacc = mfma_32x32x16(ka, qf[s], sacc);
+  }
+  const int rpos = r0 + r32;
+  if (edge) {
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int key = k0 + 8 * (v >> 2) + 4 * half + (v & 3);
+      sacc[v] = (key <= rpos && key > rpos - kWindow) ? sacc[v] : -INFINITY;
+    }
+  }
+  const float mt = max_halves(max16(sacc));
+  if (__any(mt > m_run + kRescaleThreshold)) {
+    const float m_new = fmaxf(m_run, mt);
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    l_part *= alpha;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o[i] *= alpha;
+    m_run = m_new;
+  }
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+  float l_pair[2] = {0.0f, 0.0f};
+  bf16x8 pf[2];
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt) {
+    u32x4 pk;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const bf16x2 p2 = {(__bf16)__builtin_amdgcn_exp2f(sacc[8 * tt + 2 * w] - m_run),
+                         (__bf16)__builtin_amdgcn_exp2f(sacc[8 * tt + 2 * w + 1] - m_run)};
+      l_pair[w & 1] = __builtin_amdgcn_fdot2_f32_bf16(p2, ones, l_pair[w & 1], false);
+      pk[w] = __builtin_bit_cast(uint32_t, p2);
+    }
+    pf[tt] = as_bf16x8(pk);
+  }
+  l_part += l_pair[0] + l_pair[1];
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt) {
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+      const int off = v_lane_off + 16 * tt * 512 + 64 * (db ^ vr);
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vs + off));
+      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vs + off + 8 * 512));
+      const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      o[db] = mfma_32x32x16(va, pf[tt], o[db]);
+    }
+  }
+}
+
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void prefill_split_kernel(PrefillArgs a) {
+  using T = LayerTraits<kSliding>;
+  // [band half][stage][K, V]: 128 KB; after the loop it holds the second half's O.
+  __shared__ __attribute__((aligned(1024))) uint8_t s_ring[2][2][2][kTileBytes];
+  __shared__ double s_inv[T::kRot / 2];
+  __shared__ float s_ml[kGroup][2][64];             // second half's running max and row sums, per lane
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int bh = wave >> 2, hw = wave & 3;          // band half, head within the group
+  const int half = lane >> 5, r32 = lane & 31;
+  const int units = a.batch * kKvHeads;
+  const int b = (blockIdx.x % units) / kKvHeads, g = blockIdx.x % kKvHeads;
+  const int q0 = (blockIdx.x / units) * kSplitRows;
+  const SeqSpan sp = seq_span(a, b);
+  const int S = sp.len;
+  if (q0 >= S) return;                              // whole workgroup
+  const int hq = g * kGroup + hw;
+
+  const int hi_key = min(q0 + kSplitRows - 1, S - 1);
+  const int lo_key = max(0, q0 - (kWindow - 1));
+  const int kt_lo = lo_key / kBN, n = hi_key / kBN - kt_lo + 1;
+  const int n0 = (n + 1) / 2;                       // tiles of the first half (the second: n - n0)
+  const int my_lo = bh ? kt_lo + n0 : kt_lo, my_n = bh ? n - n0 : n0;
+  uint8_t* const ring = &s_ring[bh][0][0][0];
+  // A tile of this half: the 4 waves of the half each issue the loads two waves issue in
+  // prefill_kernel (virtual waves 2 hw and 2 hw + 1).
+  auto issue = [&](int kt, int stage) {
+    uint8_t* ks = ring + stage * 2 * kTileBytes;
+    uint8_t* vs = ks + kTileBytes;
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int i = 0; i < kKLoads + kVLoads; ++i)
+        issue_one<kSliding, false>(a, b, sp, g, kt * kBN, 2 * hw + u, lane, ks, vs, i);
+  };
+  if (my_n > 0) issue(my_lo, 0);
+  if (tid < T::kRot / 2) s_inv[tid] = rope_inv_rev(tid, T::kRot, log2(T::kTheta));
+  barrier_lds();
+  bf16x8 qf[16];
+  load_q<kSliding>(a, sp, hq, q0 + r32, 0, half, s_inv, qf);
+  wait_vmcnt<0>();
+  barrier_lds();
+
+  f32x16 o[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) o[i] = f32x16{0};
+  float m_run = -1e30f, l_part = 0.0f;
+  const int grp = lane >> 4, vr = (lane >> 2) & 3, vc = lane & 3;
+  const int v_lane_off = (4 * (grp >> 1) + vr) * 512 + 16 * (2 * (grp & 1) + (vc >> 1)) + 8 * (vc & 1);
+
+  // Both halves step together (one barrier per step); the second half has n - n0 <= n0
+  // tiles and idles in its last step when n is odd.
+  for (int i = 0; i < n0; ++i) {
+    const int st = i & 1;
+    if (i + 1 < my_n) issue(my_lo + i + 1, st ^ 1);   // the stage read in step i - 1
+    if (i < my_n) {
+      const uint8_t* ks = ring + st * 2 * kTileBytes;
+      split_tile(ks, ks + kTileBytes, (my_lo + i) * kBN, q0, lane, qf, o, m_run, l_part, v_lane_off);
+    }
+    if (i + 1 < my_n) wait_vmcnt<0>();              // this lane's loads of the next tile
+    barrier_lds();
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  // The second half's state to LDS (the rings are idle now), lane-linear per wave.
+  float* const s_o = reinterpret_cast<float*>(&s_ring[0][0][0][0]);   // [4 waves][128][64] floats
+  if (bh == 1) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) s_o[(hw * 128 + 16 * i + v) * 64 + lane] = o[i][v];
+    s_ml[hw][0][lane] = m_run;
+    s_ml[hw][1][lane] = l_part;
+  }
+  barrier_lds();
+  if (bh == 0) {
+    const float m1 = s_ml[hw][0][lane], l1 = s_ml[hw][1][lane];
+    const float mm = fmaxf(m_run, m1);
+    const float a0 = __builtin_amdgcn_exp2f(m_run - mm), a1 = __builtin_amdgcn_exp2f(m1 - mm);
+    l_part = l_part * a0 + l1 * a1;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) o[i][v] = o[i][v] * a0 + s_o[(hw * 128 + 16 * i + v) * 64 + lane] * a1;
+  }
+  barrier_lds();                                    // merge reads done before the staging writes
+  if (bh == 1) return;
+
+  // Epilogue of the first half's waves: O / l * sigmoid(gate), staged through LDS (pitch
+  // 264 bytes, half the dims at a time) so that the stores write whole 256-byte row runs.
+  const int row = q0 + r32;
+  const float l_tot = l_part + __shfl_xor(l_part, 32);
+  const float gl = row < S ? bf16_to_f32(a.gate[(sp.row0 + row) * kQHeads + hq]) : 0.0f;
+  const float scale = sigmoidf_fast(gl) / l_tot;
+  constexpr int kPitch = 264;
+  uint8_t* const stage = &s_ring[0][0][0][0] + hw * (32 * kPitch);
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+#pragma unroll
+    for (int d4 = 0; d4 < 4; ++d4) {
+      const int db = 4 * r + d4;
+#pragma unroll
+      for (int qd = 0; qd < 4; ++qd) {
+        u32x2 w;
+        w[0] = pack_bf16x2(o[db][4 * qd] * scale, o[db][4 * qd + 1] * scale);
+        w[1] = pack_bf16x2(o[db][4 * qd + 2] * scale, o[db][4 * qd + 3] * scale);
+        *reinterpret_cast<u32x2*>(stage + r32 * kPitch + (32 * d4 + 8 * qd + 4 * half) * 2) = w;
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4));   // lgkmcnt(0): own writes
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int rr = 4 * i + (lane >> 4), c = lane & 15;
+      const u32x4 x = *reinterpret_cast<const u32x4*>(stage + rr * kPitch + c * 16);
+      const int grow = q0 + rr;
+      if (grow < S)
+        *reinterpret_cast<u32x4*>(a.out + ((sp.row0 + grow) * kQHeads + hq) * kHeadDim + 128 * r + 8 * c) = x;
+    }
+    __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4));   // reads done before reuse
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
 }  // namespace
 
 hipError_t launch_prefill(int layer_type, const PrefillArgs& a, hipStream_t stream) {
@@ -625,6 +828,13 @@ hipError_t launch_prefill(int layer_type, const PrefillArgs& a, hipStream_t stre
   const dim3 rope_grid((unsigned)(((size_t)a.seq_len * kKvHeads * 32 + 255) / 256), (unsigned)a.batch);
   if (layer_type == kSliding) {
     hipLaunchKernelGGL(prefill_rope_kernel<kSliding>, rope_grid, dim3(256), 0, stream, a);
+    // Too few 64-row blocks to fill the chip's 256 CUs: 32-row blocks with the key band
+    // split over two wave groups (batches without a cached prefix, uniform lengths).
+    if (a.start_pos == 0 && a.cu_seqlens == nullptr && blocks < 256) {
+      const int nqb32 = (a.seq_len + kSplitRows - 1) / kSplitRows;
+      hipLaunchKernelGGL(prefill_split_kernel, dim3(nqb32 * a.batch * kKvHeads), dim3(kThreads), 0, stream, a);
+      return hipGetLastError();
+    }
     if (a.start_pos > 0)
       hipLaunchKernelGGL((prefill_kernel<kSliding, true>), dim3(blocks), dim3(kThreads), 0, stream, a);
     else

@@ -196,8 +196,10 @@ size_t spark_attn_prefill_varlen_workspace_bytes(int32_t layer_type, int32_t tot
  *   workspace    >= spark_attn_prefill_varlen_workspace_bytes(layer_type, total_tokens),
  *                256-byte aligned
  * 1 <= batch <= 65535, 1 <= max_seqlen <= 2^20, batch * max_seqlen < 2^32,
- * total_tokens >= 1.  The per-row arithmetic is spark_attn_prefill's: a sequence's
- * outputs are bit for bit those of a batch-1 call on that sequence.  The attention
+ * total_tokens >= 1.  The per-row arithmetic is spark_attn_prefill's: on FULL layers a
+ * sequence's outputs are bit for bit those of a batch-1 call on that sequence; a short
+ * SLIDING batch-1 call (fewer than 256 blocks of 64 rows x 4 KV heads) splits each key band
+ * over two wave groups, so there the two agree up to rounding.  The attention
  * workgroups take their query blocks from a queue in the workspace (latest blocks first on
  * FULL layers), which the RoPE launch resets, so that unequal lengths still spread evenly
  * over the XCDs; calls sharing a workspace must be ordered on a stream.

@@ -39,8 +39,10 @@ def test_varlen_all_rows(fga, lt, lens):
 
 @pytest.mark.parametrize("lt", [oracle.SLIDING, oracle.FULL], ids=["sliding", "full"])
 def test_varlen_equals_single_sequence_calls(fga, lt):
-    """Each sequence's rows are bit for bit those of a batch-1 prefill of that sequence:
-    the same tiles in the same order, only the row offsets differ."""
+    """Each sequence's rows are those of a batch-1 prefill of that sequence.  Full layers:
+    bit for bit (the same tiles in the same order, only the row offsets differ).  Sliding
+    layers: a batch-1 call this short splits each key band over two wave groups and merges
+    them, so the rounding differs; the rows must agree to the parity bar."""
     import torch
     lens = [700, 0, 1, 1100, 33, 64]
     x, cu = _packed(8100 + lt, lens)
@@ -52,8 +54,12 @@ def test_varlen_equals_single_sequence_calls(fga, lt):
         one = fga.prefill(lt, *(to_dev(x[k][sl][None]) for k in ("q", "k", "v", "gate")))
         torch.cuda.synchronize()
         ref = bits_of(one)[0]
-        nd = int((got[sl] != ref).sum())
-        assert nd == 0, f"sequence {b}: {nd} output elements differ from its batch-1 call"
+        if lt == oracle.FULL:
+            nd = int((got[sl] != ref).sum())
+            assert nd == 0, f"sequence {b}: {nd} output elements differ from its batch-1 call"
+        else:
+            f = lambda u: (u.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+            assert_parity(f(got[sl]), f(ref), f"sequence {b} against its batch-1 call")
 
 
 @pytest.mark.parametrize("lt", [oracle.SLIDING, oracle.FULL], ids=["sliding", "full"])
