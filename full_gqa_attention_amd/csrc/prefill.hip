@@ -634,20 +634,29 @@ constexpr int kSplitLoads = 2 * (kKLoads + kVLoads);   // load instructions per 
 
 // One tile (keys k0 .. k0 + 31, K in ks, V in vs) for the 32 rows starting at position r0,
 // lane row r32: S^T = K Q^T, band mask on edge tiles, lazy online softmax, O^T += V^T P^T.
-// The same arithmetic as a step of prefill_kernel (whose prefetches are interleaved).
+// The same arithmetic as a step of prefill_kernel.  load(j), j = 0 .. 7, issues the j-th
+// load instruction of the next tile: one every two QK MFMAs (back to back, a tile's loads
+// stall every wave of the CU on the texture unit's queue), or all at once when no row of
+// the block sees this tile.
+template <class Load>
 __device__ __forceinline__ void split_tile(const uint8_t* ks, const uint8_t* vs, int k0, int r0, int lane,
                                            const bf16x8 (&qf)[16], f32x16 (&o)[8], float& m_run, float& l_part,
-                                           int v_lane_off) {
+                                           int v_lane_off, Load load) {
   const int half = lane >> 5, r32 = lane & 31;
   const int vr = (lane >> 2) & 3;
   const bool any = (k0 <= r0 + 31) && (k0 + kBN - 1 >= r0 - (kWindow - 1));
-  if (!any) return;                                  // wave-uniform: no row of the block sees the tile
+  if (!any) {                                        // wave-uniform: no row of the block sees the tile
+#pragma unroll
+    for (int j = 0; j < kSplitLoads; ++j) load(j);
+    return;
+  }
   const bool edge = (k0 + kBN - 1 > r0) || (k0 < r0 + 31 - (kWindow - 1));
   f32x16 sacc = f32x16{0};
 #pragma unroll
   for (int s = 0; s < 16; ++s) {
     const bf16x8 ka = as_bf16x8(*reinterpret_cast<const u32x4*>(ks + (32 * (2 * s + half) + r32) * 16));
     sacc = mfma_32x32x16(ka, qf[s], sacc);
+    if (s & 1) load(s >> 1);
   }
   const int rpos = r0 + r32;
   if (edge) {
@@ -721,18 +730,16 @@ void prefill_split_kernel(PrefillArgs a) {
   const int n0 = (n + 1) / 2;                       // tiles of the first half (the second: n - n0)
   const int my_lo = bh ? kt_lo + n0 : kt_lo, my_n = bh ? n - n0 : n0;
   uint8_t* const ring = &s_ring[bh][0][0][0];
-  // A tile of this half: the 4 waves of the half each issue the loads two waves issue in
-  // prefill_kernel (virtual waves 2 hw and 2 hw + 1).
-  auto issue = [&](int kt, int stage) {
+  // Load j of a tile of this half: the 4 waves of the half each issue the loads two waves
+  // issue in prefill_kernel (virtual waves 2 hw and 2 hw + 1).
+  auto issue_j = [&](int kt, int stage, int j) {
     uint8_t* ks = ring + stage * 2 * kTileBytes;
-    uint8_t* vs = ks + kTileBytes;
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-      for (int i = 0; i < kKLoads + kVLoads; ++i)
-        issue_one<kSliding, false>(a, b, sp, g, kt * kBN, 2 * hw + u, lane, ks, vs, i);
+    issue_one<kSliding, false>(a, b, sp, g, kt * kBN, 2 * hw + (j >> 2), lane, ks, ks + kTileBytes, j & 3);
   };
-  if (my_n > 0) issue(my_lo, 0);
+  if (my_n > 0) {
+#pragma unroll
+    for (int j = 0; j < kSplitLoads; ++j) issue_j(my_lo, 0, j);
+  }
   if (tid < T::kRot / 2) s_inv[tid] = rope_inv_rev(tid, T::kRot, log2(T::kTheta));
   barrier_lds();
   bf16x8 qf[16];
@@ -751,12 +758,15 @@ void prefill_split_kernel(PrefillArgs a) {
   // tiles and idles in its last step when n is odd.
   for (int i = 0; i < n0; ++i) {
     const int st = i & 1;
-    if (i + 1 < my_n) issue(my_lo + i + 1, st ^ 1);   // the stage read in step i - 1
+    const bool next = i + 1 < my_n;
     if (i < my_n) {
+      // The next tile goes into the stage read in step i - 1 (every wave passed the barrier
+      // after it).
       const uint8_t* ks = ring + st * 2 * kTileBytes;
-      split_tile(ks, ks + kTileBytes, (my_lo + i) * kBN, q0, lane, qf, o, m_run, l_part, v_lane_off);
+      split_tile(ks, ks + kTileBytes, (my_lo + i) * kBN, q0, lane, qf, o, m_run, l_part, v_lane_off,
+                 [&](int j) { if (next) issue_j(my_lo + i + 1, st ^ 1, j); });
     }
-    if (i + 1 < my_n) wait_vmcnt<0>();              // this lane's loads of the next tile
+    if (next) wait_vmcnt<0>();                      // this lane's loads of the next tile
     barrier_lds();
     __builtin_amdgcn_sched_barrier(0);
   }
