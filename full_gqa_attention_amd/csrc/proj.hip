@@ -10,8 +10,9 @@
 //     nearest even), into the workspace;
 //   * qkv_gemm_kernel: C = X_q W_q^T on v_mfma_scale_f32_32x32x64_f8f6f4 (block scales 1),
 //     output tiles of 256 tokens x 256 channels on 8 waves, K in stages of 128 bytes
-//     through an LDS ring filled by direct global->LDS loads; epilogue C * s_token * s_channel, rounded to bf16
-//     and stored straight into the q, k or v layout the attention path reads.
+//     through an LDS ring filled by direct global->LDS loads; epilogue C * s_token * s_channel, rounded to bf16,
+//     staged through LDS by rows and stored straight into the q, k or v layout the attention
+//     path reads.
 #include "spark_device.hpp"
 #include "spark_launch.hpp"
 
@@ -122,6 +123,11 @@ __device__ __forceinline__ void dma16_s(const void* sbase, uint32_t voff, void* 
 
 __device__ __forceinline__ void wait_vmcnt0() {
   __builtin_amdgcn_s_waitcnt(0 | (0x7 << 4) | (0xF << 8));   // vmcnt(0), others untouched
+}
+// This wave's LDS accesses done (its own staged writes visible to its other lanes).
+__device__ __forceinline__ void wait_lgkmcnt0() {
+  __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4));   // lgkmcnt(0), others untouched
+  __builtin_amdgcn_wave_barrier();
 }
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {                // vmcnt <= N, others untouched
@@ -249,27 +255,51 @@ __global__ __launch_bounds__(64 * WM * WN) void qkv_gemm_kernel(ProjArgs a) {
     __syncthreads();
   }
 
-  // Epilogue: C * s_token * s_channel -> bf16, into q, k or v (each tile lies in one).
+  // Epilogue: C * s_token * s_channel -> bf16, into q, k or v (each tile lies in one).  A
+  // wave's accumulators hold 2-byte pieces of rows spread over 32 lanes; stored as they are
+  // they make scattered 2-byte writes.  So each wave stages 16 rows x 128 channels at a time
+  // in LDS (the operand stages are free after the loop's last barrier) and stores whole
+  // 256-byte row pieces with 16-byte writes.
   uint16_t* dst;
   int ld, col0;
   if (n0 < kQOut) { dst = a.q; ld = kQOut; col0 = n0; }
   else if (n0 < kQOut + kKvOut) { dst = a.k; ld = kKvOut; col0 = n0 - kQOut; }
   else { dst = a.v; ld = kKvOut; col0 = n0 - kQOut - kKvOut; }
+  static_assert(BNW == 4, "a wave's tile is 128 channels: 256 bytes per staged row");
+  // Row pitch 272 bytes: rows 4 apart (the two half-waves) start 16 banks apart.
+  constexpr int kEpPitch = 272;
+  static_assert(G::kWaves * 16 * kEpPitch <= S * G::kBM * BK, "staging fits in the X stages");
+  typedef uint16_t __attribute__((may_alias)) u16_alias;
+  typedef u32x4 __attribute__((may_alias)) u32x4_alias;
+  uint8_t* const ep = &s_x[0][0] + wave * (16 * kEpPitch);
+  float sw[BNW];
 #pragma unroll
-  for (int bn = 0; bn < BNW; ++bn) {
-    const int c = 32 * (BNW * wn + bn) + r32;
-    const float sw = a.w_scale[n0 + c];
+  for (int bn = 0; bn < BNW; ++bn) sw[bn] = a.w_scale[n0 + 32 * (BNW * wn + bn) + r32];
 #pragma unroll
-    for (int bm = 0; bm < BMW; ++bm)
+  for (int bm = 0; bm < BMW; ++bm)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int row = m0 + 32 * (BMW * wm + bm) + 8 * (v >> 2) + 4 * half + (v & 3);
-        if (row < T) {
-          const float y = acc[bm][bn][v] * a.xs[row] * sw;
-          dst[(size_t)row * ld + col0 + c] = (uint16_t)(pack_bf16x2(y, 0.0f) & 0xffffu);
+    for (int p = 0; p < 2; ++p) {              // rows 16 p .. 16 p + 15 of the 32-row block
+      const int r0 = m0 + 32 * (BMW * wm + bm) + 16 * p;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {            // accumulator element 8 p + u: local row rl
+        const int rl = 8 * (u >> 2) + 4 * half + (u & 3);
+        const float xs = a.xs[min(r0 + rl, T - 1)];
+#pragma unroll
+        for (int bn = 0; bn < BNW; ++bn) {
+          const float y = acc[bm][bn][8 * p + u] * xs * sw[bn];
+          *reinterpret_cast<u16_alias*>(ep + rl * kEpPitch + 2 * (32 * bn + r32)) =
+              (uint16_t)(pack_bf16x2(y, 0.0f) & 0xffffu);
         }
       }
-  }
+      wait_lgkmcnt0();
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {            // 16 lanes per row, 4 rows per read
+        const int rl = 4 * i + (lane >> 4), cc = lane & 15;
+        const u32x4 x = *reinterpret_cast<const u32x4_alias*>(ep + rl * kEpPitch + 16 * cc);
+        if (r0 + rl < T) st_global16(dst + (size_t)(r0 + rl) * ld + col0 + 128 * wn + 8 * cc, x);
+      }
+      wait_lgkmcnt0();                         // staged rows read before the next are written
+    }
 }
 
 // 256 x 256 workgroup tiles on 4 x 2 waves of 2 x 4 blocks, two 128-byte stages.
