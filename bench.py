@@ -472,6 +472,7 @@ def w_decode_b64(ctx, steps, warmup, preheat_s):
                     check="decode_b64_sliding")
     for mode in ("warm", "cold"):
         out[f"decode_b64_sliding_{mode}"] = r[mode]
+        out[f"decode_b64_sliding_{mode}"]["traffic"] = measured_traffic("decode_sliding_b64")
         log(f"decode B=64 sliding ring, {mode}: {r[mode]['us']:.1f} us  {r[mode]['gbs']:.0f} GB/s")
     return out
 
@@ -650,7 +651,8 @@ def w_proj(ctx, steps, warmup, preheat_s):
         flops = 2 * T * 2560 * 6144
         out[f"qkv_proj_fp8_t{T}"] = {"us": ms * 1e3, "tflops_fp8": flops / (ms * 1e-3) / 1e12,
                                      "frac_fp8_mfma": flops / (ms * 1e-3) / 1e12 / PEAK_FP8_TFLOPS,
-                                     "gate_gflops_bf16": 2 * T * 2560 * 16 / 1e9}
+                                     "gate_gflops_bf16": 2 * T * 2560 * 16 / 1e9,
+                                     "traffic": measured_traffic(f"qkv_proj_fp8_t{T}")}
         log(f"FP8 q/k/v + bf16 gate projection T={T}: {ms * 1e3:.0f} us  "
             f"{flops / (ms * 1e-3) / 1e12:.0f} TFLOP/s (fp8 GEMM flops)")
         del x, w, wsc, wg, outs, wsp
