@@ -304,7 +304,7 @@ __global__ __launch_bounds__(64 * WM * WN) void qkv_gemm_kernel(ProjArgs a) {
 
 // 256 x 256 workgroup tiles on 4 x 2 waves of 2 x 4 blocks, two 128-byte stages.
 using GemmCfg = GemmShape<4, 2, 2, 4, 2, 128>;
-#define SPARK_GEMM_KERNEL qkv_gemm_kernel<4, 2, 2, 4, 2, 128>
+constexpr auto kGemmKernel = qkv_gemm_kernel<4, 2, 2, 4, 2, 128>;
 
 }  // namespace
 
@@ -316,7 +316,7 @@ size_t proj_workspace_bytes(int tokens) {
 hipError_t launch_qkv_proj(const ProjArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL(quant_gate_kernel, dim3((a.tokens + kQgTokens - 1) / kQgTokens), dim3(256), 0, stream, a);
   const int m_tiles = (a.tokens + GemmCfg::kBM - 1) / GemmCfg::kBM;
-  hipLaunchKernelGGL((SPARK_GEMM_KERNEL), dim3(m_tiles * (kQkvOut / GemmCfg::kBN)),
+  hipLaunchKernelGGL(kGemmKernel, dim3(m_tiles * (kQkvOut / GemmCfg::kBN)),
                      dim3(64 * GemmCfg::kWaves), 0, stream, a);
   return hipGetLastError();
 }
