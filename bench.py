@@ -14,7 +14,8 @@ context lengths uniform in [1024, 32768], full layer, KV GB/s against HBM peak),
 other workload under ``configs`` (each with its own roofline figures), and the CPU oracle
 (``cpu_baseline``): timed on the host's cores on a row sample of the headline stack, and
 over every output of the single-layer and decode workloads, with the GPU result's error
-against it.
+against it.  ``configs`` also holds a square bf16 GEMM of the vendor library timed on the
+same box (context for the fractions of the published MFMA peak; not part of the path).
 
 Inputs are synthetic and resident in HBM before timing starts; timing uses HIP events on
 the stream the kernels are launched on.  Every timed loop is preceded by at least
@@ -39,7 +40,7 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 PEAK_FP8_TFLOPS = 5000.0       # MI355X dense fp8 MFMA
 FLOP_PER_PAIR = 4 * 256 * 16   # QK^T + PV over the 16 query heads, per visible (query, key) pair
 WORKLOADS = ("stack", "full_s8192", "sliding_s1024", "chunk", "varlen", "decode_b64", "decode_long",
-             "decode_q8", "decode_step", "append", "proj")
+             "decode_q8", "decode_step", "append", "proj", "gemm_ref")
 
 
 def log(msg):
@@ -673,6 +674,31 @@ def copy_calibration():
                       "read_plus_write_gbs": 4 * n / (ms * 1e-3) / 1e9}), flush=True)
 
 
+def gemm_reference(preheat_s=1.0):
+    """A square bf16 GEMM from the vendor library (torch.matmul, hipBLASLt) on the same box:
+    what a dense bf16 MFMA workload reaches there, as context for the attention kernels'
+    fraction of the published peak.  Not part of the path."""
+    import torch
+    out = {}
+    for n in (8192, 16384):
+        a = torch.randn(n, n, device="cuda").bfloat16()
+        b = torch.randn(n, n, device="cuda").bfloat16()
+        c = torch.empty(n, n, device="cuda", dtype=torch.bfloat16)
+        ms, pre = time_launches(lambda: torch.matmul(a, b, out=c), 20, 5, preheat_s)
+        tf = 2 * n ** 3 / (ms * 1e-3) / 1e12
+        out[f"vendor_bf16_gemm_n{n}"] = {"ms": ms, "tflops": tf, "frac_of_peak": tf / PEAK_BF16_TFLOPS,
+                                         "preheat_s": pre, "what": "torch.matmul (hipBLASLt), context only"}
+        del a, b, c
+    torch.cuda.empty_cache()
+    return out
+
+
+def w_gemm_ref(ctx, steps, warmup, preheat_s):
+    r = gemm_reference(max(preheat_s, 0.5))
+    log("vendor bf16 GEMM: " + ", ".join(f"{k} {v['tflops']:.0f} TFLOP/s" for k, v in r.items()))
+    return r
+
+
 def kernel_source_hash(files):
     import hashlib
     h = hashlib.sha256()
@@ -705,6 +731,8 @@ def main():
     ap.add_argument("--only", default=",".join(WORKLOADS),
                     help="comma-separated subset of: " + ", ".join(WORKLOADS))
     ap.add_argument("--skip-cpu-baseline", action="store_true")
+    ap.add_argument("--gemm-reference", action="store_true",
+                    help="only time a square bf16 GEMM of the vendor library (context for the MFMA fractions)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run the 4 GiB device copy used to scale traffic counters")
     args = ap.parse_args()
@@ -725,6 +753,9 @@ def main():
     if args.copy_calibration:
         copy_calibration()
         return
+    if args.gemm_reference:
+        print(json.dumps(gemm_reference()), flush=True)
+        return
     ctx = Ctx(fga, synth, args)
     result = {
         "metric": METRIC, "value": None, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
@@ -737,7 +768,8 @@ def main():
     }
     fns = {"stack": w_stack, "full_s8192": w_full_s8192, "sliding_s1024": w_sliding_s1024, "chunk": w_chunk,
            "varlen": w_varlen, "decode_b64": w_decode_b64, "decode_long": w_decode_long,
-           "decode_q8": w_decode_q8, "decode_step": w_decode_step, "append": w_append, "proj": w_proj}
+           "decode_q8": w_decode_q8, "decode_step": w_decode_step, "append": w_append, "proj": w_proj,
+           "gemm_ref": w_gemm_ref}
     configs = {}
     for name in WORKLOADS:
         if name not in only:
