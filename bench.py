@@ -267,15 +267,18 @@ def w_stack(ctx, steps, warmup, preheat_s):
 
 
 def cpu_stack_sample(ctx, layers, S):
-    """The oracle on uniformly random rows of one full layer (3) and one sliding layer (0)
-    of the timed stack, on the same inputs, against the GPU's outputs of those rows."""
+    """The oracle on 192 rows of one full layer (3) and one sliding layer (0) of the timed
+    stack -- the edge rows 0, 1, 511, 512, 513, S/2, S-1 and uniformly random others -- on the
+    same inputs, against the GPU's outputs of those rows."""
     import numpy as np
     import oracle
     rng = np.random.default_rng(ctx.synth.SEED_STACK_S32768 + 1)
     rec = {}
+    fixed = np.array([0, 1, 511, 512, 513, S // 2, S - 1])
     for layer, n_rows in ((3, 192), (0, 192)):
         lt, q, k, v, g, o = layers[layer]
-        rows = np.sort(rng.choice(S, size=n_rows, replace=False))
+        others = np.setdiff1d(np.arange(S), fixed)
+        rows = np.sort(np.concatenate([fixed, rng.choice(others, size=n_rows - len(fixed), replace=False)]))
         inp = [host_bits(t) for t in (q, k, v, g)]
         got = f64_of(o[:, rows])
         t0 = time.perf_counter()
@@ -290,8 +293,8 @@ def cpu_stack_sample(ctx, layers, S):
 
 
 def w_full_s8192(ctx, steps, warmup, preheat_s):
-    """One full layer, S = 8192 (host-drawn inputs, as in the parity tests)."""
-    import numpy as np
+    """One full layer, S = 8192 (host-drawn inputs, as in the parity tests); the oracle over
+    every output."""
     import torch
     fga, synth = ctx.fga, ctx.synth
     S = 8192
@@ -306,10 +309,9 @@ def w_full_s8192(ctx, steps, warmup, preheat_s):
     log(f"full prefill S=8192: {ms * 1e3:.1f} us  {tf:.0f} TFLOP/s")
     if ctx.cpu:
         import oracle
-        rows = np.sort(np.random.default_rng(synth.SEED_FULL_S8192 + 1).choice(S, size=256, replace=False))
-        ctx.oracle_check("full_prefill_s8192", "256 uniformly random rows (all 16 heads)",
-                         lambda: oracle.prefill(inp["q"], inp["k"], inp["v"], inp["gate"], oracle.FULL, rows=rows),
-                         f64_of(out[:, rows]), len(rows), "rows")
+        ctx.oracle_check("full_prefill_s8192", "every output (8192 rows x 16 heads)",
+                         lambda: oracle.prefill(inp["q"], inp["k"], inp["v"], inp["gate"], oracle.FULL),
+                         f64_of(out), S, "rows")
     return {"ms": ms, "tokens_per_s": S / (ms * 1e-3), "flop": flops, "tflops": tf, "preheat_s": pre,
             "roofline": {"bound": "mfma", "achieved": tf, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                          "frac": tf / PEAK_BF16_TFLOPS, "traffic": measured_traffic("prefill_full_s8192")}}
@@ -799,9 +801,10 @@ def main():
         cb = {"value": None, "unit": "tokens/s", "cores": info["threads_used"], "kind": "oracle"}
         if getattr(ctx, "stack_cpu", None):
             cb["value"] = ctx.stack_cpu["value"]
-            cb["sample"] = ("fp64 NumPy oracle on 192 uniformly random query rows (all 16 heads) of layer 3 (full) "
-                            "and of layer 0 (sliding) of the timed S=32768 stack, on the same inputs; stack "
-                            "tokens/s extrapolated as 1 / (9 t_full_row + 27 t_sliding_row)")
+            cb["sample"] = ("fp64 NumPy oracle on 192 query rows (all 16 heads; rows 0, 1, 511, 512, 513, S/2, "
+                            "S-1 and 185 uniformly random others) of layer 3 (full) and of layer 0 (sliding) of "
+                            "the timed S=32768 stack, on the same inputs; stack tokens/s extrapolated as "
+                            "1 / (9 t_full_row + 27 t_sliding_row)")
             cb["stack_layers"] = ctx.stack_cpu["layers"]
         cb.update({k: info[k] for k in ("affinity_cores", "blas_threads", "cpu_model")})
         cb["per_workload"] = ctx.oracle_runs
