@@ -582,16 +582,24 @@ def w_decode_step(ctx, steps, warmup, preheat_s):
                 dec(lt, qd, gd, cache, sl, maxlen, out=od, workspace=wsd)
 
         ms, pre = time_launches(step, 10, 3, preheat_s)
+        # The same step captured once in a HIP graph and replayed, as a serving loop would
+        # (tests/test_gpu_graph.py checks that replays reproduce the eager calls bit for bit).
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        ms_graph, _ = time_launches(graph.replay, 10, 3, preheat_s)
         vis = int(lens.astype(np.int64).sum()) * 9 + int(np.minimum(lens, 512).astype(np.int64).sum()) * 27
         row = 2 * 4 * (512 if kv == "bf16" else 272)
         nbytes = vis * row + 36 * B * (16 * 256 * 4 + 32)
         out[f"decode_step_36_layers_b64_{kv}"] = {"ms": ms, "tokens_per_s": B / (ms * 1e-3),
                                                   "gbs": nbytes / (ms * 1e-3) / 1e9,
                                                   "frac_hbm": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                                                  "ms_graph": ms_graph, "tokens_per_s_graph": B / (ms_graph * 1e-3),
+                                                  "frac_hbm_graph": nbytes / (ms_graph * 1e-3) / 1e9 / PEAK_HBM_GBS,
                                                   "bytes": nbytes, "kv": kv}
         log(f"36-layer decode step, batch 64 ({kv} cache): {ms:.2f} ms  {B / (ms * 1e-3):.0f} tokens/s  "
-            f"{nbytes / (ms * 1e-3) / 1e9:.0f} GB/s")
-        del layers
+            f"{nbytes / (ms * 1e-3) / 1e9:.0f} GB/s; as a graph replay {ms_graph:.2f} ms")
+        del graph, layers
         torch.cuda.empty_cache()
     return out
 
