@@ -38,10 +38,12 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 constexpr int kQgTokens = 16, kQgWaves = 4;
 constexpr int kQgSlice = kHidden / kQgWaves;   // 640
 constexpr int kQgSteps = kQgSlice / 32;        // 20
+constexpr int kQgCodePitch = kQgSlice + 16;     // LDS row of a token's codes (656 = 41 x 16 bytes)
 
 __global__ __launch_bounds__(256) void quant_gate_kernel(ProjArgs a) {
   __shared__ float s_gate[kQgWaves][kQgTokens * kGates];
   __shared__ float s_max[kQgWaves][kQgTokens];
+  __shared__ __attribute__((aligned(16))) uint8_t s_codes[kQgWaves][kQgTokens][kQgCodePitch];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int t0 = blockIdx.x * kQgTokens;
   const int tr = lane & 15;
@@ -73,26 +75,59 @@ __global__ __launch_bounds__(256) void quant_gate_kernel(ProjArgs a) {
     const float g = s_gate[0][i] + s_gate[1][i] + s_gate[2][i] + s_gate[3][i];
     if (t0 + i / kGates < a.tokens) a.gate[(size_t)t0 * kGates + i] = (uint16_t)(pack_bf16x2(g, 0.0f) & 0xffffu);
   }
-  // Per-token FP8: s = max|x| / 448, codes E4M3FN(x / s), both divisions IEEE fp32.
+  // Per-token FP8: s = max|x| / 448, codes E4M3FN(x / s), both quotients IEEE fp32.  Per
+  // element, x / s is formed as q0 = x * y with y = 1 / s (one IEEE division per token) and
+  // one correction, q = q0 + (x - s q0) y in fused multiply-adds (Markstein), with x's
+  // sign: an exhaustive check over every bf16 x and every bf16 maximum
+  // (tests/test_quant_quotient.py) finds q equal to the IEEE quotient wherever
+  // |x / s| >= 2^-10 when s >= 2^-80, and below 2^-10 both give the zero code of x's sign.
+  // Tokens with a smaller scale take the division itself.  (160 IEEE divisions per lane
+  // took about half of this kernel's time.)
   const float mt = fmaxf(fmaxf(s_max[0][tr], s_max[1][tr]), fmaxf(s_max[2][tr], s_max[3][tr]));
   const float sc = mt / kE4M3Max;
-  if (t0 + tr >= a.tokens) return;
-  uint8_t* qr = a.xq + (size_t)t * kHidden + k0;
+  // A lane's codes are 8-byte pieces of its token's row, 32 bytes apart: they go to LDS
+  // first, and the wave then stores its 16 tokens x 640 bytes in 16-byte pieces that run
+  // along the rows (each store instruction writes 1 KB in at most three runs instead of 64
+  // pieces of 8 bytes).
+  uint8_t* const sc_row = &s_codes[wave][tr][8 * (lane >> 4)];
+  auto codes = [&](auto quot) {
 #pragma unroll
-  for (int s = 0; s < kQgSteps; ++s) {
-    uint32_t w[2];
+    for (int s = 0; s < kQgSteps; ++s) {
+      uint32_t w[2];
 #pragma unroll
-    for (int d = 0; d < 2; ++d) {
-      const uint32_t p0 = xv[s][2 * d], p1 = xv[s][2 * d + 1];
-      const float y0 = sc > 0.0f ? bf16_lo(p0) / sc : 0.0f, y1 = sc > 0.0f ? bf16_hi(p0) / sc : 0.0f;
-      const float y2 = sc > 0.0f ? bf16_lo(p1) / sc : 0.0f, y3 = sc > 0.0f ? bf16_hi(p1) / sc : 0.0f;
-      int pk = __builtin_amdgcn_cvt_pk_fp8_f32(y0, y1, 0, false);
-      pk = __builtin_amdgcn_cvt_pk_fp8_f32(y2, y3, pk, true);
-      w[d] = (uint32_t)pk;
+      for (int d = 0; d < 2; ++d) {
+        const uint32_t p0 = xv[s][2 * d], p1 = xv[s][2 * d + 1];
+        const float y0 = quot(bf16_lo(p0)), y1 = quot(bf16_hi(p0));
+        const float y2 = quot(bf16_lo(p1)), y3 = quot(bf16_hi(p1));
+        int pk = __builtin_amdgcn_cvt_pk_fp8_f32(y0, y1, 0, false);
+        pk = __builtin_amdgcn_cvt_pk_fp8_f32(y2, y3, pk, true);
+        w[d] = (uint32_t)pk;
+      }
+      *reinterpret_cast<u32x2*>(sc_row + 32 * s) = u32x2{w[0], w[1]};
     }
-    *reinterpret_cast<u32x2*>(qr + 32 * s) = u32x2{w[0], w[1]};
+  };
+  if (sc >= 0x1p-80f) {
+    const float ry = 1.0f / sc;
+    codes([&](float x) {
+      const float q0 = __fmul_rn(x, ry);
+      // x's sign restored: for x = -0 the sums give +0, where x / s is -0 (code 0x80).
+      return __builtin_copysignf(__builtin_fmaf(__builtin_fmaf(-sc, q0, x), ry, q0), x);
+    });
+  } else {
+    codes([&](float x) { return sc > 0.0f ? x / sc : 0.0f; });
   }
-  if (wave == 0 && lane < kQgTokens) a.xs[t] = sc;
+  // This wave's LDS writes are done before its reads (one wave's LDS operations execute in
+  // order; the barrier keeps the compiler from moving them).
+  __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4));   // lgkmcnt(0)
+  __builtin_amdgcn_wave_barrier();
+  constexpr int kChunks = kQgSlice / 16;         // 40 pieces of 16 bytes per token
+#pragma unroll
+  for (int i = 0; i < kQgTokens * kChunks / 64; ++i) {
+    const int f = 64 * i + lane, tok = f / kChunks, c = f % kChunks;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(&s_codes[wave][tok][16 * c]);
+    if (t0 + tok < a.tokens) st_global16(a.xq + (size_t)(t0 + tok) * kHidden + wave * kQgSlice + 16 * c, v);
+  }
+  if (wave == 0 && lane < kQgTokens && t0 + tr < a.tokens) a.xs[t] = sc;
 }
 
 // ---------------------------------------------------------------------------------------
