@@ -38,7 +38,9 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 constexpr int kQgTokens = 16, kQgWaves = 4;
 constexpr int kQgSlice = kHidden / kQgWaves;   // 640
 constexpr int kQgSteps = kQgSlice / 32;        // 20
-constexpr int kQgCodePitch = kQgSlice + 16;     // LDS row of a token's codes (656 = 41 x 16 bytes)
+// LDS row of a token's codes: 784 bytes = 3 x 256 + 16, so that the 8-byte writes of 16
+// tokens x 2 lanes (half a wave) fall on 64 distinct banks.
+constexpr int kQgCodePitch = kQgSlice + 144;
 
 __global__ __launch_bounds__(256) void quant_gate_kernel(ProjArgs a) {
   __shared__ float s_gate[kQgWaves][kQgTokens * kGates];
