@@ -196,19 +196,19 @@ def test_decode_batch_beyond_plan_threads(fga, num_parts):
 RING_LENS = [0, 1, 5, 31, 32, 33, 255, 256, 257, 480, 511, 512, 513, 700, 1000, 2049, 17, 300, 64, 96]
 
 
-def test_sliding_ring_batch_edges(fga):
-    """A batch of 20 on a sliding layer (the one-launch ring kernel, used from batch 16 on):
-    an empty sequence, ragged chunks, waves whose second chunk is empty, partly filled and
-    full, and rings holding more positions than the window."""
-    lens = np.array(RING_LENS, np.int32)
-    B = len(lens)
+@pytest.mark.parametrize("B", [15, 16, 20])
+def test_sliding_ring_batch_edges(fga, B):
+    """Batches of 15, 16 and 20 on a sliding layer (split + merge below batch 16, the
+    one-launch ring kernel from 16 on): an empty sequence, ragged chunks, waves whose second
+    chunk is empty, partly filled and full, and rings holding more positions than the window."""
+    lens = np.array(RING_LENS[:B], np.int32)
     d = synth.decode_inputs(4400, B, int(lens.max()), fill_lens=lens)
     rk, rv = _ring_from_contiguous(d["cache_k"], d["cache_v"], lens)
     got = _decode_dev(fga, oracle.SLIDING, d, rk, rv, lens)
     live = lens > 0
     assert np.all(got[~live] == 0.0)
     want = oracle.decode(d["q"][live], d["gate"][live], rk[live], rv[live], lens[live], oracle.SLIDING)
-    assert_parity(got[live], want, "decode sliding ring, batch 20 of edge lengths")
+    assert_parity(got[live], want, f"decode sliding ring, batch {B} of edge lengths")
 
 
 def test_sliding_ring_is_deterministic(fga):

@@ -17,8 +17,10 @@ def _run(fga, inp, lt, cache=None):
     return out
 
 
+# Sliding layers without a prefix take the split-band kernel while batch x ceil(S/64) x 4 < 256
+# (B3 S1300: 252 blocks; B1 S4032: 252) and the 64-row kernel from 256 on (B4 S1000, B1 S4033).
 SMALL = [(1, 1), (1, 2), (2, 63), (1, 64), (1, 65), (2, 100), (1, 511), (1, 512), (1, 513),
-         (1, 700), (2, 1100)]
+         (1, 700), (2, 1100), (3, 1300), (4, 1000), (1, 4032), (1, 4033)]
 
 
 @pytest.mark.parametrize("lt", [oracle.SLIDING, oracle.FULL], ids=["sliding", "full"])
