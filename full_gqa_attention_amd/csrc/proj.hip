@@ -296,7 +296,8 @@ __global__ __launch_bounds__(64 * WM * WN) void qkv_gemm_kernel(ProjArgs a) {
   // wave's accumulators hold 2-byte pieces of rows spread over 32 lanes; stored as they are
   // they make scattered 2-byte writes.  So each wave stages 16 rows x 128 channels at a time
   // in LDS (the operand stages are free after the loop's last barrier) and stores whole
-  // 256-byte row pieces with 16-byte writes.
+  // 256-byte row pieces with 16-byte non-temporal writes (the outputs are not read again by
+  // this kernel; measured 8% faster for the whole call at 32768 tokens than plain stores).
   uint16_t* dst;
   int ld, col0;
   if (n0 < kQOut) { dst = a.q; ld = kQOut; col0 = n0; }
@@ -333,7 +334,8 @@ __global__ __launch_bounds__(64 * WM * WN) void qkv_gemm_kernel(ProjArgs a) {
       for (int i = 0; i < 4; ++i) {            // 16 lanes per row, 4 rows per read
         const int rl = 4 * i + (lane >> 4), cc = lane & 15;
         const u32x4 x = *reinterpret_cast<const u32x4_alias*>(ep + rl * kEpPitch + 16 * cc);
-        if (r0 + rl < T) st_global16(dst + (size_t)(r0 + rl) * ld + col0 + 128 * wn + 8 * cc, x);
+        if (r0 + rl < T)
+          __builtin_nontemporal_store(x, reinterpret_cast<u32x4*>(dst + (size_t)(r0 + rl) * ld + col0 + 128 * wn + 8 * cc));
       }
       wait_lgkmcnt0();                         // staged rows read before the next are written
     }
