@@ -108,6 +108,26 @@ __device__ __forceinline__ void barrier_lds() {
 constexpr int kKLoads = 16 / kWaves;              // K-tile load instructions per wave
 constexpr int kVLoads = 16 / kWaves;              // V-tile load instructions per wave
 
+// The K tile layout of the short-sequence kernels (prefill_split_kernel): 16 blocks of
+// 1 KB, block 8 ch + jb holding keys 4 jb .. 4 jb + 3, its 16-byte slot 16 r + t key
+// 4 jb + r, chunk 16 ch + (t ^ (key & 15)).  One load instruction then fills a block from
+// four contiguous 256-byte half rows, where the chunk-major layout of prefill_kernel reads
+// 32 rows x 32 bytes per instruction, twice the cache lines (measured: the short kernels'
+// tile loads took a sixth of their time; the long band of prefill_kernel hides them); the
+// XOR spreads the 32 keys of one chunk over all banks for the MFMA operand reads.
+// Byte offset, from the tile's first row, that lane reads for block n (rows past lim, the
+// tile's last readable row, read that row instead).
+__device__ __forceinline__ uint32_t kswz_src(int n, int lane, int lim) {
+  const int r = lane >> 4, t = lane & 15;
+  const int j = 4 * (n & 7) + r;
+  const int c = 16 * (n >> 3) + (t ^ (j & 15));
+  return (uint32_t)(min(j, lim) * 2048 + 16 * c);
+}
+// Byte offset in the tile of key r32's chunk c (c = 2 s + half: the MFMA A operand of step s).
+__device__ __forceinline__ int kswz_read(int c, int r32) {
+  return 8192 * (c >> 4) + 1024 * (r32 >> 2) + 256 * (r32 & 3) + 16 * ((c & 15) ^ (r32 & 15));
+}
+
 // Global rows of key position p (p < P + n) of (sequence b, KV head g): the cached prefix
 // for p < P (slot p, or ring slot p mod 512 on a sliding layer), else the chunk's keys as
 // rotated by the RoPE pass and its values.
@@ -147,9 +167,10 @@ __device__ __forceinline__ size_t chunk_row(const SeqSpan& sp, int g, int p, int
 // the MFMA operand reads could use.  With a prefix, a tile wholly inside the prefix or
 // wholly inside the chunk picks its source once and only a tile across start_pos selects
 // per lane; there the scalar-base form was 2-5% slower (both forms in one kernel).
-template <int LT, bool PFX>
+template <int LT, bool PFX, bool KSWZ = false>
 __device__ __forceinline__ void issue_one(const PrefillArgs& a, int b, const SeqSpan& sp, int g, int k0,
                                           int wave, int lane, uint8_t* ks, uint8_t* vs, int i) {
+  static_assert(!(KSWZ && PFX), "the swizzled K layout is for calls without a prefix");
   const int P = PFX ? a.start_pos : 0;
   const int kend = P + sp.len;
   const bool in_chunk = !PFX || k0 >= P, in_prefix = k0 + kBN <= P;   // wave-uniform
@@ -159,8 +180,13 @@ __device__ __forceinline__ void issue_one(const PrefillArgs& a, int b, const Seq
     const int lim = kend - 1 - k0;                  // last readable row of the tile
     const size_t base = (((sp.row0 + k0) * kKvHeads + g) * kHeadDim) * 2;   // bytes
     if (i < kKLoads) {
-      const uint8_t* src = (const uint8_t*)a.k_rot + base + 64 * wave;
-      dma16_s(src, (uint32_t)(min(l31, lim) * 2048 + 16 * h + 32 * i), ks + (kKLoads * wave + i) * 1024);
+      if constexpr (KSWZ) {
+        const int n = kKLoads * wave + i;
+        dma16_s((const uint8_t*)a.k_rot + base, kswz_src(n, lane, lim), ks + n * 1024);
+      } else {
+        const uint8_t* src = (const uint8_t*)a.k_rot + base + 64 * wave;
+        dma16_s(src, (uint32_t)(min(l31, lim) * 2048 + 16 * h + 32 * i), ks + (kKLoads * wave + i) * 1024);
+      }
     } else {
       const int j = i - kKLoads;
       const uint8_t* src = (const uint8_t*)a.v + base;
@@ -335,6 +361,26 @@ __device__ __forceinline__ void load_q(const PrefillArgs& a, const SeqSpan& sp, 
       qf[s] = as_bf16x8(y);
     }
   }
+}
+
+// Rotate and scale one rotary pair of Q fragments, the arithmetic of load_q's pair step:
+// x1 holds dims m0 .. m0 + 7, x2 the dims r/2 further on, at position p.
+__device__ __forceinline__ void rotate_q_pair(const u32x4& x1, const u32x4& x2, double p, const double* inv,
+                                              int m0, bf16x8& q1, bf16x8& q2) {
+  u32x4 y1, y2;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    float c0, s0, c1, s1;
+    const int m = m0 + 2 * w;
+    rope_cos_sin(p, inv[m], c0, s0);
+    rope_cos_sin(p, inv[m + 1], c1, s1);
+    const float a0 = bf16_lo(x1[w]), a1 = bf16_hi(x1[w]);
+    const float b0 = bf16_lo(x2[w]), b1 = bf16_hi(x2[w]);
+    y1[w] = pack_bf16x2((a0 * c0 - b0 * s0) * kQScale, (a1 * c1 - b1 * s1) * kQScale);
+    y2[w] = pack_bf16x2((b0 * c0 + a0 * s0) * kQScale, (b1 * c1 + a1 * s1) * kQScale);
+  }
+  q1 = as_bf16x8(y1);
+  q2 = as_bf16x8(y2);
 }
 
 template <int LT, bool PFX>
@@ -625,23 +671,32 @@ void prefill_kernel(PrefillArgs a) {
 // Sliding layers of short sequences, whose 64-row query blocks cannot fill the chip (at
 // S = 1024: 16 blocks x 4 KV heads = 64 workgroups for 256 CUs, each walking up to 18
 // dependent tiles).  Here a workgroup takes 32 query positions of one (sequence, KV head)
-// and its 8 waves are the 4 query heads times the two halves of the key band: wave w
-// computes head 4g + w % 4 over the tiles of half w / 4, so the dependent chain is at most
-// 9 tiles and twice as many workgroups run.  Each half streams its tiles through its own
-// two-stage ring (prefetch one tile ahead); at the end the second half's (max, sum, O) go
-// through LDS to the wave of the same head in the first half, which merges them with
-// log-sum-exp weights and runs the usual gated epilogue.
+// and its waves are HPW query heads times the two halves of the key band: wave w computes
+// head w % HPW of its share over the tiles of half w / HPW, so the dependent chain is at
+// most 9 tiles.  HPW = 4 (8 waves, the whole group) gives twice as many workgroups as the
+// 64-row kernel; HPW = 2 (4 waves, one per SIMD, each K/V tile loaded by two workgroups)
+// four times as many, for grids that would otherwise leave CUs idle.  Each half streams
+// its tiles through its own two-stage ring (prefetch one tile ahead; the ring's 128 KB
+// allow one workgroup per CU); at the end the second half's (max, sum, O) go through LDS
+// to the wave of the same head in the first half, which merges them with log-sum-exp
+// weights and runs the usual gated epilogue.
 
 constexpr int kSplitRows = 32;                       // query positions per workgroup
-constexpr int kSplitLoads = 2 * (kKLoads + kVLoads);   // load instructions per wave and tile
+// Up to this many workgroups of 4 query heads, the workgroups take 2 heads each instead
+// (twice as many workgroups of 4 waves).
+constexpr int kSplitHalfGroupMaxWgs = 128;
+// Load instructions per wave and tile when HPW waves share a half's tiles (a tile is 32
+// instructions of 1 KB).
+template <int HPW>
+constexpr int split_loads() { return 32 / HPW; }
 
 // One tile (keys k0 .. k0 + 31, K in ks, V in vs) for the 32 rows starting at position r0,
 // lane row r32: S^T = K Q^T, band mask on edge tiles, lazy online softmax, O^T += V^T P^T.
-// The same arithmetic as a step of prefill_kernel.  load(j), j = 0 .. 7, issues the j-th
-// load instruction of the next tile: one every two QK MFMAs (back to back, a tile's loads
-// stall every wave of the CU on the texture unit's queue), or all at once when no row of
-// the block sees this tile.
-template <class Load>
+// The same arithmetic as a step of prefill_kernel.  load(j), j = 0 .. NL - 1, issues the
+// j-th load instruction of the next tile: spread evenly over the 16 QK MFMAs (back to
+// back, a tile's loads stall every wave of the CU on the texture unit's queue), or all at
+// once when no row of the block sees this tile.
+template <int NL, class Load>
 __device__ __forceinline__ void split_tile(const uint8_t* ks, const uint8_t* vs, int k0, int r0, int lane,
                                            const bf16x8 (&qf)[16], f32x16 (&o)[8], float& m_run, float& l_part,
                                            int v_lane_off, Load load) {
@@ -650,16 +705,17 @@ __device__ __forceinline__ void split_tile(const uint8_t* ks, const uint8_t* vs,
   const bool any = (k0 <= r0 + 31) && (k0 + kBN - 1 >= r0 - (kWindow - 1));
   if (!any) {                                        // wave-uniform: no row of the block sees the tile
 #pragma unroll
-    for (int j = 0; j < kSplitLoads; ++j) load(j);
+    for (int j = 0; j < NL; ++j) load(j);
     return;
   }
   const bool edge = (k0 + kBN - 1 > r0) || (k0 < r0 + 31 - (kWindow - 1));
   f32x16 sacc = f32x16{0};
 #pragma unroll
   for (int s = 0; s < 16; ++s) {
-    const bf16x8 ka = as_bf16x8(*reinterpret_cast<const u32x4*>(ks + (32 * (2 * s + half) + r32) * 16));
+    const bf16x8 ka = as_bf16x8(*reinterpret_cast<const u32x4*>(ks + kswz_read(2 * s + half, r32)));
     sacc = mfma_32x32x16(ka, qf[s], sacc);
-    if (s & 1) load(s >> 1);
+    constexpr int kEvery = 16 / NL;
+    if (s % kEvery == kEvery - 1) load(s / kEvery);
   }
   const int rpos = r0 + r32;
   if (edge) {
@@ -707,9 +763,162 @@ __device__ __forceinline__ void split_tile(const uint8_t* ks, const uint8_t* vs,
   }
 }
 
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+// MFMAs of the one-wave-per-SIMD tile step, in asm so that the register classes are ours:
+// the Q fragments (the B operand of S^T = K Q^T, read-only in the loop) in AGPRs, the
+// accumulators S^T and O^T, the K, V and P fragments in VGPRs -- which leaves VGPRs for
+// fragments read several MFMAs ahead.  Left to itself the compiler puts the accumulators
+// in AGPRs, and moves blocks of O between the two register files around every MFMA
+// sequence.
+//
+// The compiler adds no wait states around asm, so the asm carries them: 11 between an
+// 8-pass 32x32x16 MFMA (gfx950) and a VALU read of its result (S^T), a few between a VALU
+// write and an MFMA read (the P fragments).  Back-to-back accumulation into the same
+// registers needs none.
+template <bool FIRST, bool LAST>
+__device__ __forceinline__ void mfma_qk_asm(f32x16& acc, bf16x8 k, const bf16x8& q) {
+  if constexpr (FIRST)
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(k), "a"(q));
+  else if constexpr (LAST)
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\ts_nop 7\n\ts_nop 4" : "+v"(acc) : "v"(k), "a"(q));
+  else
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(k), "a"(q));
+}
+template <bool AFTER_VALU>
+__device__ __forceinline__ void mfma_pv_asm(f32x16& acc, bf16x8 v, bf16x8 p) {
+  if constexpr (AFTER_VALU)
+    asm volatile("s_nop 4\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(v), "v"(p));
+  else
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(v), "v"(p));
+}
+// The wait states between the last PV MFMA of the loop and the first VALU read of O after
+// it, tied to O so that no read moves above them.
+__device__ __forceinline__ void mfma_result_fence(f32x16 (&o)[8]) {
+  asm volatile("s_nop 7\n\ts_nop 4"
+               : "+v"(o[0]), "+v"(o[1]), "+v"(o[2]), "+v"(o[3]), "+v"(o[4]), "+v"(o[5]), "+v"(o[6]), "+v"(o[7]));
+}
+// 16 fragments of 16 bytes, 1 KB apart in LDS from p, straight into AGPRs (complete when
+// the asm ends), so that the Q fragments are born in the register file they stay in.
+__device__ __forceinline__ void lds_read16_agpr(const void* p, bf16x8 (&q)[16]) {
+  const uint32_t a = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+  asm volatile("ds_read_b128 %0, %16\n\tds_read_b128 %1, %16 offset:1024\n\t"
+               "ds_read_b128 %2, %16 offset:2048\n\tds_read_b128 %3, %16 offset:3072\n\t"
+               "ds_read_b128 %4, %16 offset:4096\n\tds_read_b128 %5, %16 offset:5120\n\t"
+               "ds_read_b128 %6, %16 offset:6144\n\tds_read_b128 %7, %16 offset:7168\n\t"
+               "ds_read_b128 %8, %16 offset:8192\n\tds_read_b128 %9, %16 offset:9216\n\t"
+               "ds_read_b128 %10, %16 offset:10240\n\tds_read_b128 %11, %16 offset:11264\n\t"
+               "ds_read_b128 %12, %16 offset:12288\n\tds_read_b128 %13, %16 offset:13312\n\t"
+               "ds_read_b128 %14, %16 offset:14336\n\tds_read_b128 %15, %16 offset:15360\n\t"
+               "s_waitcnt lgkmcnt(0)"
+               : "=a"(q[0]), "=a"(q[1]), "=a"(q[2]), "=a"(q[3]), "=a"(q[4]), "=a"(q[5]), "=a"(q[6]), "=a"(q[7]),
+                 "=a"(q[8]), "=a"(q[9]), "=a"(q[10]), "=a"(q[11]), "=a"(q[12]), "=a"(q[13]), "=a"(q[14]),
+                 "=a"(q[15])
+               : "v"(a)
+               : "memory");
+}
+
+// split_tile for workgroups of one wave per SIMD (HPW = 2), where no other wave hides a
+// wave's own LDS latency: fragments are read several MFMAs ahead of their use (the
+// register file of a lone wave holds them), so no MFMA waits on a read issued just
+// before it.  The next tile's 16 loads go one after each QK MFMA, unconditionally (the
+// caller gives a harmless tile when there is none): a branch among the MFMAs would end the
+// scheduling region, and with it the early reads.
+template <class Load>
+__device__ __forceinline__ void split_tile_deep(const uint8_t* ks, const uint8_t* vs, int k0, int r0, int lane,
+                                                const bf16x8 (&qf)[16], f32x16 (&o)[8], float& m_run,
+                                                float& l_part, int v_lane_off, Load load) {
+  const int half = lane >> 5, r32 = lane & 31;
+  const int vr = (lane >> 2) & 3;
+  const bool any = (k0 <= r0 + 31) && (k0 + kBN - 1 >= r0 - (kWindow - 1));
+  if (!any) {                                        // wave-uniform: no row of the block sees the tile
+#pragma unroll
+    for (int j = 0; j < 16; ++j) load(j);
+    return;
+  }
+  const bool edge = (k0 + kBN - 1 > r0) || (k0 < r0 + 31 - (kWindow - 1));
+  auto read_k = [&](int s) { return as_bf16x8(*reinterpret_cast<const u32x4*>(ks + kswz_read(2 * s + half, r32))); };
+  auto read_v = [&](int tt, int db) {
+    const int off = v_lane_off + 16 * tt * 512 + 64 * (db ^ vr);
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vs + off));
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vs + off + 8 * 512));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+  // K fragments eight ahead of their MFMA, V fragments of the first 16 keys during the
+  // softmax and of the second 16 during the first half of the PV MFMAs.
+  bf16x8 ka[16];
+#pragma unroll
+  for (int s = 0; s < 8; ++s) ka[s] = read_k(s);
+  f32x16 sacc;
+#pragma unroll
+  for (int s = 0; s < 16; ++s) {
+    if (s == 0)
+      mfma_qk_asm<true, false>(sacc, ka[s], qf[s]);
+    else if (s == 15)
+      mfma_qk_asm<false, true>(sacc, ka[s], qf[s]);
+    else
+      mfma_qk_asm<false, false>(sacc, ka[s], qf[s]);
+    if (s + 8 < 16) ka[s + 8] = read_k(s + 8);
+    load(s);
+  }
+  bf16x8 va[2][8];
+#pragma unroll
+  for (int db = 0; db < 8; ++db) va[0][db] = read_v(0, db);
+  const int rpos = r0 + r32;
+  if (edge) {
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int key = k0 + 8 * (v >> 2) + 4 * half + (v & 3);
+      sacc[v] = (key <= rpos && key > rpos - kWindow) ? sacc[v] : -INFINITY;
+    }
+  }
+  const float mt = max_halves(max16(sacc));
+  if (__any(mt > m_run + kRescaleThreshold)) {
+    const float m_new = fmaxf(m_run, mt);
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    l_part *= alpha;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o[i] *= alpha;
+    m_run = m_new;
+  }
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+  float l_pair[2] = {0.0f, 0.0f};
+  bf16x8 pf[2];
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt) {
+    u32x4 pk;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const bf16x2 p2 = {(__bf16)__builtin_amdgcn_exp2f(sacc[8 * tt + 2 * w] - m_run),
+                         (__bf16)__builtin_amdgcn_exp2f(sacc[8 * tt + 2 * w + 1] - m_run)};
+      l_pair[w & 1] = __builtin_amdgcn_fdot2_f32_bf16(p2, ones, l_pair[w & 1], false);
+      pk[w] = __builtin_bit_cast(uint32_t, p2);
+    }
+    pf[tt] = as_bf16x8(pk);
+  }
+  l_part += l_pair[0] + l_pair[1];
+#pragma unroll
+  for (int db = 0; db < 8; ++db) {
+    if (db == 0)
+      mfma_pv_asm<true>(o[db], va[0][db], pf[0]);
+    else
+      mfma_pv_asm<false>(o[db], va[0][db], pf[0]);
+    va[1][db] = read_v(1, db);
+  }
+#pragma unroll
+  for (int db = 0; db < 8; ++db) {
+    if (db == 0)
+      mfma_pv_asm<true>(o[db], va[1][db], pf[1]);
+    else
+      mfma_pv_asm<false>(o[db], va[1][db], pf[1]);
+  }
+}
+
+template <int HPW>
+__global__ __launch_bounds__(128 * HPW) __attribute__((amdgpu_waves_per_eu(HPW / 2, HPW / 2)))
 void prefill_split_kernel(PrefillArgs a) {
   using T = LayerTraits<kSliding>;
+  static_assert(HPW == 2 || HPW == 4, "query heads per workgroup");
+  constexpr int kParts = kGroup / HPW;              // workgroups per (block, KV head)
+  constexpr int kNL = split_loads<HPW>();
   // [band half][stage][K, V]: 128 KB; after the loop it holds the second half's O.
   __shared__ __attribute__((aligned(1024))) uint8_t s_ring[2][2][2][kTileBytes];
   __shared__ double s_inv[T::kRot / 2];
@@ -717,15 +926,16 @@ void prefill_split_kernel(PrefillArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int bh = wave >> 2, hw = wave & 3;          // band half, head within the group
+  const int bh = wave / HPW, hw = wave % HPW;      // band half, head within the workgroup
   const int half = lane >> 5, r32 = lane & 31;
-  const int units = a.batch * kKvHeads;
-  const int b = (blockIdx.x % units) / kKvHeads, g = blockIdx.x % kKvHeads;
+  const int units = a.batch * kKvHeads * kParts;
+  const int u = blockIdx.x % units;
+  const int part = u % kParts, g = (u / kParts) % kKvHeads, b = u / (kParts * kKvHeads);
   const int q0 = (blockIdx.x / units) * kSplitRows;
   const SeqSpan sp = seq_span(a, b);
   const int S = sp.len;
   if (q0 >= S) return;                              // whole workgroup
-  const int hq = g * kGroup + hw;
+  const int hq = g * kGroup + part * HPW + hw;
 
   const int hi_key = min(q0 + kSplitRows - 1, S - 1);
   const int lo_key = max(0, q0 - (kWindow - 1));
@@ -733,20 +943,54 @@ void prefill_split_kernel(PrefillArgs a) {
   const int n0 = (n + 1) / 2;                       // tiles of the first half (the second: n - n0)
   const int my_lo = bh ? kt_lo + n0 : kt_lo, my_n = bh ? n - n0 : n0;
   uint8_t* const ring = &s_ring[bh][0][0][0];
-  // Load j of a tile of this half: the 4 waves of the half each issue the loads two waves
-  // issue in prefill_kernel (virtual waves 2 hw and 2 hw + 1).
+  // Load j of a tile of this half: the HPW waves of the half each issue the loads of
+  // 8 / HPW of prefill_kernel's waves (virtual waves (8 / HPW) hw + j / 4).
   auto issue_j = [&](int kt, int stage, int j) {
     uint8_t* ks = ring + stage * 2 * kTileBytes;
-    issue_one<kSliding, false>(a, b, sp, g, kt * kBN, 2 * hw + (j >> 2), lane, ks, ks + kTileBytes, j & 3);
+    issue_one<kSliding, false, true>(a, b, sp, g, kt * kBN, (8 / HPW) * hw + (j >> 2), lane, ks, ks + kTileBytes, j & 3);
   };
   if (my_n > 0) {
 #pragma unroll
-    for (int j = 0; j < kSplitLoads; ++j) issue_j(my_lo, 0, j);
+    for (int j = 0; j < kNL; ++j) issue_j(my_lo, 0, j);
   }
-  if (tid < T::kRot / 2) s_inv[tid] = rope_inv_rev(tid, T::kRot, log2(T::kTheta));
-  barrier_lds();
   bf16x8 qf[16];
-  load_q<kSliding>(a, sp, hq, q0 + r32, 0, half, s_inv, qf);
+  uint16_t gate_raw = 0;                            // HPW = 2: loaded here, used by the epilogue
+  if constexpr (HPW == 2) {
+    // The two waves of a head (the band halves) each load and rotate half of its Q
+    // fragments, the rotary pairs (s, s + 8) for s in [4 bh, 4 bh + 4) (sliding layers
+    // rotate all 256 dims), into LDS -- the first half's second ring stage, idle until the
+    // first step issues its loads -- and both read all 16 back, into AGPRs.  The loads go
+    // out before the frequency table is computed, which hides part of their latency.
+    static_assert(T::kRot == kHeadDim, "every Q fragment is in a rotary pair");
+    // Rows past the sequence's end read its last row (their outputs are never stored):
+    // loads under a branch would be waited for at the branch's end.
+    const int row = q0 + r32, rowc = min(row, S - 1);
+    const uint16_t* qrow = a.q + ((sp.row0 + rowc) * kQHeads + hq) * kHeadDim;
+    u32x4 qr[8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      qr[j] = ld_global16(qrow + 16 * (4 * bh + j) + 8 * half);
+      qr[4 + j] = ld_global16(qrow + 16 * (4 * bh + j + 8) + 8 * half);
+    }
+    gate_raw = a.gate[(sp.row0 + rowc) * kQHeads + hq];
+    if (tid < T::kRot / 2) s_inv[tid] = rope_inv_rev(tid, T::kRot, log2(T::kTheta));
+    barrier_lds();
+    uint8_t* const qs = &s_ring[0][1][0][0] + hw * kTileBytes;   // [fragment][lane] x 16 B per head
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int sf = 4 * bh + j;
+      bf16x8 y1, y2;
+      rotate_q_pair(qr[j], qr[4 + j], (double)row, s_inv, 16 * sf + 8 * half, y1, y2);
+      *reinterpret_cast<bf16x8*>(qs + (sf * 64 + lane) * 16) = y1;
+      *reinterpret_cast<bf16x8*>(qs + ((sf + 8) * 64 + lane) * 16) = y2;
+    }
+    barrier_lds();
+    lds_read16_agpr(qs + lane * 16, qf);
+  } else {
+    if (tid < T::kRot / 2) s_inv[tid] = rope_inv_rev(tid, T::kRot, log2(T::kTheta));
+    barrier_lds();
+    load_q<kSliding>(a, sp, hq, q0 + r32, 0, half, s_inv, qf);
+  }
   wait_vmcnt<0>();
   barrier_lds();
 
@@ -761,26 +1005,34 @@ void prefill_split_kernel(PrefillArgs a) {
   // tiles and idles in its last step when n is odd.
   for (int i = 0; i < n0; ++i) {
     const int st = i & 1;
-    const bool next = i + 1 < my_n;
     if (i < my_n) {
       // The next tile goes into the stage read in step i - 1 (every wave passed the barrier
-      // after it).
+      // after it).  The last step loads its own tile there again, unused: a conditional
+      // load would put branches among the QK MFMAs.
+      const int kt_next = min(my_lo + i + 1, my_lo + my_n - 1);
       const uint8_t* ks = ring + st * 2 * kTileBytes;
-      split_tile(ks, ks + kTileBytes, (my_lo + i) * kBN, q0, lane, qf, o, m_run, l_part, v_lane_off,
-                 [&](int j) { if (next) issue_j(my_lo + i + 1, st ^ 1, j); });
+      auto ld = [&](int j) { issue_j(kt_next, st ^ 1, j); };
+      if constexpr (HPW == 2)
+        split_tile_deep(ks, ks + kTileBytes, (my_lo + i) * kBN, q0, lane, qf, o, m_run, l_part, v_lane_off, ld);
+      else
+        split_tile<kNL>(ks, ks + kTileBytes, (my_lo + i) * kBN, q0, lane, qf, o, m_run, l_part, v_lane_off, ld);
+      wait_vmcnt<0>();                              // this lane's loads (also before the merge reuses the rings)
     }
-    if (next) wait_vmcnt<0>();                      // this lane's loads of the next tile
     barrier_lds();
     __builtin_amdgcn_sched_barrier(0);
   }
 
-  // The second half's state to LDS (the rings are idle now), lane-linear per wave.
-  float* const s_o = reinterpret_cast<float*>(&s_ring[0][0][0][0]);   // [4 waves][128][64] floats
+  if constexpr (HPW == 2) mfma_result_fence(o);
+  // The second half's state to LDS (the rings are idle now), 16 bytes per lane and
+  // lane-linear per wave.
+  f32x4* const s_o = reinterpret_cast<f32x4*>(&s_ring[0][0][0][0]);   // [HPW waves][32][64] x 16 B
   if (bh == 1) {
 #pragma unroll
     for (int i = 0; i < 8; ++i)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) s_o[(hw * 128 + 16 * i + v) * 64 + lane] = o[i][v];
+      for (int qd = 0; qd < 4; ++qd)
+        s_o[(hw * 32 + 4 * i + qd) * 64 + lane] =
+            f32x4{o[i][4 * qd], o[i][4 * qd + 1], o[i][4 * qd + 2], o[i][4 * qd + 3]};
     s_ml[hw][0][lane] = m_run;
     s_ml[hw][1][lane] = l_part;
   }
@@ -793,7 +1045,11 @@ void prefill_split_kernel(PrefillArgs a) {
 #pragma unroll
     for (int i = 0; i < 8; ++i)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) o[i][v] = o[i][v] * a0 + s_o[(hw * 128 + 16 * i + v) * 64 + lane] * a1;
+      for (int qd = 0; qd < 4; ++qd) {
+        const f32x4 x = s_o[(hw * 32 + 4 * i + qd) * 64 + lane];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[i][4 * qd + e] = o[i][4 * qd + e] * a0 + x[e] * a1;
+      }
   }
   barrier_lds();                                    // merge reads done before the staging writes
   if (bh == 1) return;
@@ -803,7 +1059,8 @@ void prefill_split_kernel(PrefillArgs a) {
   // (non-temporal, as in the 64-row kernel's sliding epilogue: 2% faster here).
   const int row = q0 + r32;
   const float l_tot = l_part + __shfl_xor(l_part, 32);
-  const float gl = row < S ? bf16_to_f32(a.gate[(sp.row0 + row) * kQHeads + hq]) : 0.0f;
+  const float gl = HPW == 2 ? bf16_to_f32(gate_raw)
+                            : row < S ? bf16_to_f32(a.gate[(sp.row0 + row) * kQHeads + hq]) : 0.0f;
   const float scale = sigmoidf_fast(gl) / l_tot;
   constexpr int kPitch = 264;
   uint8_t* const stage = &s_ring[0][0][0][0] + hw * (32 * kPitch);
@@ -847,7 +1104,11 @@ hipError_t launch_prefill(int layer_type, const PrefillArgs& a, hipStream_t stre
     // split over two wave groups (batches without a cached prefix, uniform lengths).
     if (a.start_pos == 0 && a.cu_seqlens == nullptr && blocks < 256) {
       const int nqb32 = (a.seq_len + kSplitRows - 1) / kSplitRows;
-      hipLaunchKernelGGL(prefill_split_kernel, dim3(nqb32 * a.batch * kKvHeads), dim3(kThreads), 0, stream, a);
+      const int wgs = nqb32 * a.batch * kKvHeads;   // workgroups of the whole-group form
+      if (wgs <= kSplitHalfGroupMaxWgs)
+        hipLaunchKernelGGL(prefill_split_kernel<2>, dim3(2 * wgs), dim3(256), 0, stream, a);
+      else
+        hipLaunchKernelGGL(prefill_split_kernel<4>, dim3(wgs), dim3(512), 0, stream, a);
       return hipGetLastError();
     }
     if (a.start_pos > 0)
