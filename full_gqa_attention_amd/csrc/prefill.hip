@@ -682,9 +682,15 @@ void prefill_kernel(PrefillArgs a) {
 // weights and runs the usual gated epilogue.
 
 constexpr int kSplitRows = 32;                       // query positions per workgroup
-// Up to this many workgroups of 4 query heads, the workgroups take 2 heads each instead
-// (twice as many workgroups of 4 waves).
-constexpr int kSplitHalfGroupMaxWgs = 128;
+// Whether the workgroups take 2 query heads each (twice as many workgroups of 4 waves)
+// rather than 4, given the 4-head grid: both run one workgroup per CU, a round of 2-head
+// workgroups in about 0.6 of the time of a round of 4-head ones (measured at S = 512 ..
+// 4032), so the 2-head form wins while it needs at most 1.5 times as many rounds.
+constexpr int kCUs = 256;
+__host__ inline bool split_two_heads(int wgs4) {
+  const int rounds4 = (wgs4 + kCUs - 1) / kCUs, rounds2 = (2 * wgs4 + kCUs - 1) / kCUs;
+  return 2 * rounds2 <= 3 * rounds4;
+}
 // Load instructions per wave and tile when HPW waves share a half's tiles (a tile is 32
 // instructions of 1 KB).
 template <int HPW>
@@ -1102,10 +1108,10 @@ hipError_t launch_prefill(int layer_type, const PrefillArgs& a, hipStream_t stre
     hipLaunchKernelGGL(prefill_rope_kernel<kSliding>, rope_grid, dim3(256), 0, stream, a);
     // Too few 64-row blocks to fill the chip's 256 CUs: 32-row blocks with the key band
     // split over two wave groups (batches without a cached prefix, uniform lengths).
-    if (a.start_pos == 0 && a.cu_seqlens == nullptr && blocks < 256) {
+    if (a.start_pos == 0 && a.cu_seqlens == nullptr && blocks < kCUs) {
       const int nqb32 = (a.seq_len + kSplitRows - 1) / kSplitRows;
       const int wgs = nqb32 * a.batch * kKvHeads;   // workgroups of the whole-group form
-      if (wgs <= kSplitHalfGroupMaxWgs)
+      if (split_two_heads(wgs))
         hipLaunchKernelGGL(prefill_split_kernel<2>, dim3(2 * wgs), dim3(256), 0, stream, a);
       else
         hipLaunchKernelGGL(prefill_split_kernel<4>, dim3(wgs), dim3(512), 0, stream, a);

@@ -19,6 +19,9 @@ def _run(fga, inp, lt, cache=None):
 
 # Sliding layers without a prefix take the split-band kernel while batch x ceil(S/64) x 4 < 256
 # (B3 S1300: 252 blocks; B1 S4032: 252) and the 64-row kernel from 256 on (B4 S1000, B1 S4033).
+# The split kernel's workgroups take 2 query heads up to B1 S1024 and at B2 S1100 (280
+# four-head workgroups: 2 rounds of 256 CUs against 3 for the 2-head form), 4 at B3 S1300
+# and B1 S4032 (492 and 504: 2 rounds against 4).
 SMALL = [(1, 1), (1, 2), (2, 63), (1, 64), (1, 65), (2, 100), (1, 511), (1, 512), (1, 513),
          (1, 700), (2, 1100), (3, 1300), (4, 1000), (1, 4032), (1, 4033)]
 
@@ -91,10 +94,11 @@ def test_prefill_writes_cache(fga, lt, S):
     assert_parity(f64_of(out), want, f"prefill+cache lt={lt} S={S}")
 
 
-@pytest.mark.parametrize("B,S", [(1, 1024), (2, 1100)], ids=["B1S1024", "B2S1100"])
+@pytest.mark.parametrize("B,S", [(1, 1024), (2, 1100), (1, 4032)], ids=["B1S1024", "B2S1100", "B1S4032"])
 def test_short_sliding_prefill_is_deterministic(fga, B, S):
     """Short sliding layers run with the key band split over two wave groups whose states
-    meet in LDS: repeated calls are bit-identical (fresh NaN-filled buffers each call)."""
+    meet in LDS, in workgroups of 2 query heads (B1S1024, B2S1100) or 4 (B1S4032):
+    repeated calls are bit-identical (fresh NaN-filled buffers each call)."""
     import torch
     inp = synth.prefill_inputs(4343 + S, B, S)
     q, k, v, g = (to_dev(inp[n]) for n in ("q", "k", "v", "gate"))
