@@ -928,7 +928,7 @@ void prefill_split_kernel(PrefillArgs a) {
   // [band half][stage][K, V]: 128 KB; after the loop it holds the second half's O.
   __shared__ __attribute__((aligned(1024))) uint8_t s_ring[2][2][2][kTileBytes];
   __shared__ double s_inv[T::kRot / 2];
-  __shared__ float s_ml[kGroup][2][64];             // second half's running max and row sums, per lane
+  __shared__ float s_ml[kGroup][2][2][64];          // [head][half][max, row sums][lane]
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1029,57 +1029,56 @@ void prefill_split_kernel(PrefillArgs a) {
   }
 
   if constexpr (HPW == 2) mfma_result_fence(o);
-  // The second half's state to LDS (the rings are idle now), 16 bytes per lane and
-  // lane-linear per wave.
-  f32x4* const s_o = reinterpret_cast<f32x4*>(&s_ring[0][0][0][0]);   // [HPW waves][32][64] x 16 B
-  if (bh == 1) {
+  // The halves split the rest: the first stores dims 0 .. 127 (blocks 0 .. 3 of O), the
+  // second dims 128 .. 255.  Each hands the other its (max, row sums) and the four blocks
+  // the other stores, through LDS (the rings are idle now; 16 bytes per lane,
+  // lane-linear), merges the four it keeps with the partner's by log-sum-exp weights and
+  // runs the gated epilogue on them.
+  f32x4* const s_o = reinterpret_cast<f32x4*>(&s_ring[0][0][0][0]);   // [half][HPW][16][64] x 16 B
+  auto exchange = [&](auto keep_tag) {
+    constexpr int kKeep = decltype(keep_tag)::value, kGive = 4 - kKeep;
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int qd = 0; qd < 4; ++qd)
-        s_o[(hw * 32 + 4 * i + qd) * 64 + lane] =
-            f32x4{o[i][4 * qd], o[i][4 * qd + 1], o[i][4 * qd + 2], o[i][4 * qd + 3]};
-    s_ml[hw][0][lane] = m_run;
-    s_ml[hw][1][lane] = l_part;
-  }
-  barrier_lds();
-  if (bh == 0) {
-    const float m1 = s_ml[hw][0][lane], l1 = s_ml[hw][1][lane];
+        s_o[((bh * HPW + hw) * 16 + 4 * i + qd) * 64 + lane] =
+            f32x4{o[kGive + i][4 * qd], o[kGive + i][4 * qd + 1], o[kGive + i][4 * qd + 2], o[kGive + i][4 * qd + 3]};
+    s_ml[hw][bh][0][lane] = m_run;
+    s_ml[hw][bh][1][lane] = l_part;
+    barrier_lds();
+    const float m1 = s_ml[hw][1 - bh][0][lane], l1 = s_ml[hw][1 - bh][1][lane];
     const float mm = fmaxf(m_run, m1);
     const float a0 = __builtin_amdgcn_exp2f(m_run - mm), a1 = __builtin_amdgcn_exp2f(m1 - mm);
     l_part = l_part * a0 + l1 * a1;
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int qd = 0; qd < 4; ++qd) {
-        const f32x4 x = s_o[(hw * 32 + 4 * i + qd) * 64 + lane];
+        const f32x4 x = s_o[(((1 - bh) * HPW + hw) * 16 + 4 * i + qd) * 64 + lane];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) o[i][4 * qd + e] = o[i][4 * qd + e] * a0 + x[e] * a1;
+        for (int e = 0; e < 4; ++e) o[kKeep + i][4 * qd + e] = o[kKeep + i][4 * qd + e] * a0 + x[e] * a1;
       }
-  }
-  barrier_lds();                                    // merge reads done before the staging writes
-  if (bh == 1) return;
-
-  // Epilogue of the first half's waves: O / l * sigmoid(gate), staged through LDS (pitch
-  // 264 bytes, half the dims at a time) so that the stores write whole 256-byte row runs
-  // (non-temporal, as in the 64-row kernel's sliding epilogue: 2% faster here).
-  const int row = q0 + r32;
-  const float l_tot = l_part + __shfl_xor(l_part, 32);
-  const float gl = HPW == 2 ? bf16_to_f32(gate_raw)
-                            : row < S ? bf16_to_f32(a.gate[(sp.row0 + row) * kQHeads + hq]) : 0.0f;
-  const float scale = sigmoidf_fast(gl) / l_tot;
-  constexpr int kPitch = 264;
-  uint8_t* const stage = &s_ring[0][0][0][0] + hw * (32 * kPitch);
-#pragma unroll
-  for (int r = 0; r < 2; ++r) {
+    barrier_lds();                                  // merge reads done before the staging writes
+  };
+  // Epilogue: O / l * sigmoid(gate) for this half's 128 dims, staged through LDS (pitch 264
+  // bytes) so that the stores write whole 256-byte row runs (non-temporal, as in the
+  // 64-row kernel's sliding epilogue: 2% faster here).
+  auto epilogue = [&](auto keep_tag) {
+    constexpr int kKeep = decltype(keep_tag)::value;
+    const int row = q0 + r32;
+    const float l_tot = l_part + __shfl_xor(l_part, 32);
+    const float gl = HPW == 2 ? bf16_to_f32(gate_raw)
+                              : row < S ? bf16_to_f32(a.gate[(sp.row0 + row) * kQHeads + hq]) : 0.0f;
+    const float scale = sigmoidf_fast(gl) / l_tot;
+    constexpr int kPitch = 264;
+    uint8_t* const stage = &s_ring[0][0][0][0] + (bh * HPW + hw) * (32 * kPitch);
 #pragma unroll
     for (int d4 = 0; d4 < 4; ++d4) {
-      const int db = 4 * r + d4;
 #pragma unroll
       for (int qd = 0; qd < 4; ++qd) {
         u32x2 w;
-        w[0] = pack_bf16x2(o[db][4 * qd] * scale, o[db][4 * qd + 1] * scale);
-        w[1] = pack_bf16x2(o[db][4 * qd + 2] * scale, o[db][4 * qd + 3] * scale);
+        w[0] = pack_bf16x2(o[kKeep + d4][4 * qd] * scale, o[kKeep + d4][4 * qd + 1] * scale);
+        w[1] = pack_bf16x2(o[kKeep + d4][4 * qd + 2] * scale, o[kKeep + d4][4 * qd + 3] * scale);
         *reinterpret_cast<u32x2*>(stage + r32 * kPitch + (32 * d4 + 8 * qd + 4 * half) * 2) = w;
       }
     }
@@ -1092,10 +1091,15 @@ void prefill_split_kernel(PrefillArgs a) {
       const int grow = q0 + rr;
       if (grow < S)
         __builtin_nontemporal_store(x, reinterpret_cast<u32x4*>(a.out + ((sp.row0 + grow) * kQHeads + hq) * kHeadDim +
-                                                             128 * r + 8 * c));
+                                                             32 * kKeep + 8 * c));
     }
-    __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4));   // reads done before reuse
-    __builtin_amdgcn_wave_barrier();
+  };
+  if (bh == 0) {
+    exchange(std::integral_constant<int, 0>{});
+    epilogue(std::integral_constant<int, 0>{});
+  } else {
+    exchange(std::integral_constant<int, 4>{});
+    epilogue(std::integral_constant<int, 4>{});
   }
 }
 
