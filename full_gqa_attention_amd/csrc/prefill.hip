@@ -492,8 +492,12 @@ void prefill_kernel(PrefillArgs a) {
     const int k0 = kt * kBN;
     const bool two_ahead = kt + 2 <= kt_hi;
     // Steps 1 and 2 issue tile kt+2 one load every four QK MFMAs (issuing a tile's loads
-    // back to back stalls every wave of the CU on the texture unit's queue); step 0
-    // issues it after its MFMAs, which measured slightly faster than interleaving there.
+    // back to back stalls every wave of the CU on the texture unit's queue); on full layers
+    // unconditionally: past the last tile they reload it into the idle stage, unused.  A
+    // conditional load among the MFMAs ends a scheduling region every four MFMAs (1.2-1.9%
+    // slower on full layers; on sliding layers, with their short bands, the same change
+    // measured 0-1% slower and is not made).  Step 0 issues its prefetch after its MFMAs,
+    // which measured slightly faster than interleaving there.
 
     // Which row blocks see any key of this tile (wave-uniform).
     bool any[kRowBlocks], edge[kRowBlocks], any_rb = false;
@@ -513,7 +517,9 @@ void prefill_kernel(PrefillArgs a) {
         const bf16x8 ka = as_bf16x8(*reinterpret_cast<const u32x4*>(ks + (32 * (2 * s + half) + r32) * 16));
 #pragma unroll
         for (int rb = 0; rb < kRowBlocks; ++rb) sacc[rb] = mfma_32x32x16(ka, qf[rb][s], sacc[rb]);
-        if (ST != 0 && two_ahead && (s & 3) == 1) issue_one<LT, PFX>(a, b, sp, g, k0 + 2 * kBN, wave, lane, ks2, vs2, s >> 2);
+        if (ST != 0 && (LT == kFull || two_ahead) && (s & 3) == 1)
+          issue_one<LT, PFX>(a, b, sp, g, LT == kFull ? min(kt + 2, kt_hi) * kBN : k0 + 2 * kBN, wave, lane, ks2,
+                             vs2, s >> 2);
       }
       bf16x8 pf[kRowBlocks][2];
 #pragma unroll
@@ -588,6 +594,9 @@ void prefill_kernel(PrefillArgs a) {
     step(std::integral_constant<int, 2>{}, kt);
     if (++kt > kt_hi) break;
   }
+  // Full layers: the last step's reloads may still be in flight; done before the workgroup
+  // ends.
+  if constexpr (!T::kWindowed) wait_vmcnt<0>();
 
   // ---- epilogue: O / l * sigmoid(gate), bf16
   if constexpr (T::kWindowed) {
