@@ -90,6 +90,21 @@ __device__ __forceinline__ float max16(const f32x16& x) {
   return __builtin_fmaxf(a, d);
 }
 
+// The same with the NaN-propagating maximum, which gfx950 has as a three-input instruction
+// that needs no canonicalising of its inputs (the IEEE maximum above gets a v_max_f32 x, x
+// for the first two).
+__device__ __forceinline__ float maximum16(const f32x16& x) {
+  auto mx = [](float p, float q) { return __builtin_elementwise_maximum(p, q); };
+  float a = mx(mx(x[0], x[1]), x[2]);
+  float b = mx(mx(x[3], x[4]), x[5]);
+  float c = mx(mx(x[6], x[7]), x[8]);
+  float d = mx(mx(x[9], x[10]), x[11]);
+  float e = mx(mx(x[12], x[13]), x[14]);
+  a = mx(mx(a, b), c);
+  d = mx(mx(d, e), x[15]);
+  return mx(a, d);
+}
+
 // max(x, x of lane l ^ 32): v_permlane32_swap hands every lane the values of lanes l % 32
 // and 32 + l % 32, i.e. its own and its partner's.
 __device__ __forceinline__ float max_halves(float x) {
@@ -462,13 +477,20 @@ void prefill_kernel(PrefillArgs a) {
   wait_vmcnt<0>();
   barrier_lds();
 
+  // Running maximum c of each row.  Full layers without a prefix start their QK MFMAs from
+  // -c, so that the common step exponentiates the MFMA results directly (the subtractions
+  // leave the path from the QK MFMAs to the PV MFMAs), and rescale when a score beats c by
+  // more than kRescaleThreshold.  The other forms keep c = -1e30 until their first key and
+  // subtract c from the scores: the same change measured 2.7% slower on sliding layers, and
+  // the prefix form, whose per-tile source choice needs registers of its own, would spill.
+  constexpr bool kRel = !T::kWindowed && !PFX;
   f32x16 o[kRowBlocks][8];
-  float m_run[kRowBlocks], l_part[kRowBlocks];
+  float c_run[kRowBlocks], l_part[kRowBlocks];
 #pragma unroll
   for (int rb = 0; rb < kRowBlocks; ++rb) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) o[rb][i] = f32x16{0};
-    m_run[rb] = -1e30f;
+    c_run[rb] = kRel ? 0.0f : -1e30f;
     l_part[rb] = 0.0f;
   }
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
@@ -511,7 +533,7 @@ void prefill_kernel(PrefillArgs a) {
     if (any_rb) {
       f32x16 sacc[kRowBlocks];
 #pragma unroll
-      for (int rb = 0; rb < kRowBlocks; ++rb) sacc[rb] = f32x16{0};
+      for (int rb = 0; rb < kRowBlocks; ++rb) sacc[rb] = kRel ? -c_run[rb] : 0.0f;
 #pragma unroll
       for (int s = 0; s < 16; ++s) {
         const bf16x8 ka = as_bf16x8(*reinterpret_cast<const u32x4*>(ks + (32 * (2 * s + half) + r32) * 16));
@@ -534,16 +556,33 @@ void prefill_kernel(PrefillArgs a) {
             sacc[rb][v] = vis ? sacc[rb][v] : -INFINITY;
           }
         }
-        const float mt = max_halves(max16(sacc[rb]));
         float l_pair[kRowBlocks][2] = {};   // two independent row-sum chains
-        if (__any(mt > m_run[rb] + kRescaleThreshold)) {
-          const float m_new = fmaxf(m_run[rb], mt);
-          const float alpha = __builtin_amdgcn_exp2f(m_run[rb] - m_new);
+        if constexpr (!kRel) {
+          const float mt = max_halves(max16(sacc[rb]));
+          if (__any(mt > c_run[rb] + kRescaleThreshold)) {
+            const float m_new = fmaxf(c_run[rb], mt);
+            const float alpha = __builtin_amdgcn_exp2f(c_run[rb] - m_new);
+            l_part[rb] *= alpha;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) o[rb][i] *= alpha;
+            c_run[rb] = m_new;
+          }
+        } else if (const float mt = maximum16(sacc[rb]); kt == kt_lo || __any(mt > kRescaleThreshold)) {
+          // The decision needs only this lane's half of the row (its partner lane is in the
+          // same wave); the row's maximum is formed when the wave rescales.  The first tile
+          // holds key 0, which every row sees: it sets the maximum (c = 0 before it).
+          const float m_old = kt == kt_lo ? -1e30f : c_run[rb];
+          const float m_new = fmaxf(m_old, max_halves(mt) + c_run[rb]);
+          const float alpha = __builtin_amdgcn_exp2f(m_old - m_new);
           l_part[rb] *= alpha;
 #pragma unroll
           for (int i = 0; i < 8; ++i) o[rb][i] *= alpha;
-          m_run[rb] = m_new;
+          const float d = m_new - c_run[rb];      // scores relative to the new maximum
+#pragma unroll
+          for (int v = 0; v < 16; ++v) sacc[rb][v] -= d;
+          c_run[rb] = m_new;
         }
+        const float off = kRel ? 0.0f : c_run[rb];   // x - 0.0f folds to x
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
           u32x4 pk;
@@ -551,8 +590,8 @@ void prefill_kernel(PrefillArgs a) {
           for (int w = 0; w < 4; ++w) {
             // The pair is built as bf16x2 and then stored into pk, not read back out of
             // pk: hipcc (ROCm 7.2) folds a bf16x2 bit-cast of pk[w] to pk[0] for every w.
-            const bf16x2 p2 = {(__bf16)__builtin_amdgcn_exp2f(sacc[rb][8 * tt + 2 * w] - m_run[rb]),
-                               (__bf16)__builtin_amdgcn_exp2f(sacc[rb][8 * tt + 2 * w + 1] - m_run[rb])};
+            const bf16x2 p2 = {(__bf16)__builtin_amdgcn_exp2f(sacc[rb][8 * tt + 2 * w] - off),
+                               (__bf16)__builtin_amdgcn_exp2f(sacc[rb][8 * tt + 2 * w + 1] - off)};
             l_pair[rb][w & 1] = __builtin_amdgcn_fdot2_f32_bf16(p2, ones, l_pair[rb][w & 1], false);
             pk[w] = __builtin_bit_cast(uint32_t, p2);
           }
