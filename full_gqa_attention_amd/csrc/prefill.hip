@@ -42,6 +42,9 @@ constexpr int kRowBlocks = 8 / kWaves;            // 32-row blocks per wave
 constexpr int kThreads = 64 * kWaves;
 constexpr int kTileBytes = kBN * kHeadDim * 2;   // 16 KB per K or V tile
 constexpr float kRescaleThreshold = 8.0f;        // log2 units
+constexpr int kKAhead = 4;                        // full layers: K fragments read ahead
+// Instruction classes of __builtin_amdgcn_sched_group_barrier's mask.
+constexpr int kSchedMfma = 0x008, kSchedDsRead = 0x100;
 constexpr float kQScale = 0.0625f * 1.4426950408889634f;   // 1/sqrt(256) * log2(e)
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
@@ -534,14 +537,41 @@ void prefill_kernel(PrefillArgs a) {
       f32x16 sacc[kRowBlocks];
 #pragma unroll
       for (int rb = 0; rb < kRowBlocks; ++rb) sacc[rb] = kRel ? -c_run[rb] : 0.0f;
+      if constexpr (kRel) {
+        // K fragments read kKAhead MFMAs ahead, in an order pinned by scheduling groups: left
+        // to itself the scheduler sinks each read to just before its MFMA, two at a time.
+        auto kfrag = [&](int s) {
+          return as_bf16x8(*reinterpret_cast<const u32x4*>(ks + (32 * (2 * s + half) + r32) * 16));
+        };
+        bf16x8 kb[kKAhead];
 #pragma unroll
-      for (int s = 0; s < 16; ++s) {
-        const bf16x8 ka = as_bf16x8(*reinterpret_cast<const u32x4*>(ks + (32 * (2 * s + half) + r32) * 16));
+        for (int j = 0; j < kKAhead; ++j) kb[j] = kfrag(j);
 #pragma unroll
-        for (int rb = 0; rb < kRowBlocks; ++rb) sacc[rb] = mfma_32x32x16(ka, qf[rb][s], sacc[rb]);
-        if (ST != 0 && (LT == kFull || two_ahead) && (s & 3) == 1)
-          issue_one<LT, PFX>(a, b, sp, g, LT == kFull ? min(kt + 2, kt_hi) * kBN : k0 + 2 * kBN, wave, lane, ks2,
-                             vs2, s >> 2);
+        for (int s = 0; s < 16; ++s) {
+          const bf16x8 ka = kb[s % kKAhead];
+          if (s + kKAhead < 16) kb[s % kKAhead] = kfrag(s + kKAhead);
+#pragma unroll
+          for (int rb = 0; rb < kRowBlocks; ++rb) sacc[rb] = mfma_32x32x16(ka, qf[rb][s], sacc[rb]);
+          if (ST != 0 && (s & 3) == 1)
+            issue_one<LT, PFX>(a, b, sp, g, min(kt + 2, kt_hi) * kBN, wave, lane, ks2, vs2, s >> 2);
+        }
+#pragma unroll
+        for (int j = 0; j < kKAhead; ++j) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+#pragma unroll
+        for (int s = 0; s < 16; ++s) {
+          __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+          if (s + kKAhead < 16) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+        }
+      } else {
+#pragma unroll
+        for (int s = 0; s < 16; ++s) {
+          const bf16x8 ka = as_bf16x8(*reinterpret_cast<const u32x4*>(ks + (32 * (2 * s + half) + r32) * 16));
+#pragma unroll
+          for (int rb = 0; rb < kRowBlocks; ++rb) sacc[rb] = mfma_32x32x16(ka, qf[rb][s], sacc[rb]);
+          if (ST != 0 && (LT == kFull || two_ahead) && (s & 3) == 1)
+            issue_one<LT, PFX>(a, b, sp, g, LT == kFull ? min(kt + 2, kt_hi) * kBN : k0 + 2 * kBN, wave, lane, ks2,
+                               vs2, s >> 2);
+        }
       }
       bf16x8 pf[kRowBlocks][2];
 #pragma unroll
@@ -609,6 +639,15 @@ void prefill_kernel(PrefillArgs a) {
           const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
           for (int rb = 0; rb < kRowBlocks; ++rb) o[rb][db] = mfma_32x32x16(va, pf[rb][tt], o[rb][db]);
+        }
+      }
+      if constexpr (kRel) {
+        // V fragments (two transposing reads each) read two MFMAs ahead, pinned likewise.
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4, 1);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 1);
+          if (i + 2 < 16) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 1);
         }
       }
     }
