@@ -487,6 +487,8 @@ void prefill_kernel(PrefillArgs a) {
   // subtract c from the scores: the same change measured 2.7% slower on sliding layers, and
   // the prefix form, whose per-tile source choice needs registers of its own, would spill.
   constexpr bool kRel = !T::kWindowed && !PFX;
+  // Forms without a prefix read K and V fragments ahead in a pinned order (below).
+  constexpr bool kPin = !PFX;
   f32x16 o[kRowBlocks][8];
   float c_run[kRowBlocks], l_part[kRowBlocks];
 #pragma unroll
@@ -517,12 +519,12 @@ void prefill_kernel(PrefillArgs a) {
     const int k0 = kt * kBN;
     const bool two_ahead = kt + 2 <= kt_hi;
     // Steps 1 and 2 issue tile kt+2 one load every four QK MFMAs (issuing a tile's loads
-    // back to back stalls every wave of the CU on the texture unit's queue); on full layers
-    // unconditionally: past the last tile they reload it into the idle stage, unused.  A
-    // conditional load among the MFMAs ends a scheduling region every four MFMAs (1.2-1.9%
-    // slower on full layers; on sliding layers, with their short bands, the same change
-    // measured 0-1% slower and is not made).  Step 0 issues its prefetch after its MFMAs,
-    // which measured slightly faster than interleaving there.
+    // back to back stalls every wave of the CU on the texture unit's queue); without a
+    // prefix unconditionally: past the last tile they reload it into the idle stage, unused.
+    // A conditional load among the MFMAs ends a scheduling region every four MFMAs (1.2-1.9%
+    // slower on full layers; on sliding layers it measured 0-1% faster until the fragment
+    // reads were pinned, which needs one region).  Step 0 issues its prefetch after its
+    // MFMAs, which measured slightly faster than interleaving there.
 
     // Which row blocks see any key of this tile (wave-uniform).
     bool any[kRowBlocks], edge[kRowBlocks], any_rb = false;
@@ -537,9 +539,12 @@ void prefill_kernel(PrefillArgs a) {
       f32x16 sacc[kRowBlocks];
 #pragma unroll
       for (int rb = 0; rb < kRowBlocks; ++rb) sacc[rb] = kRel ? -c_run[rb] : 0.0f;
-      if constexpr (kRel) {
+      if constexpr (kPin) {
         // K fragments read kKAhead MFMAs ahead, in an order pinned by scheduling groups: left
         // to itself the scheduler sinks each read to just before its MFMA, two at a time.
+        // The tile loads go in unconditionally (sliding layers too): a branch here would end
+        // the scheduling region every four MFMAs; past the last tile they reload it into
+        // the idle stage, unused, and are waited for before the epilogue.
         auto kfrag = [&](int s) {
           return as_bf16x8(*reinterpret_cast<const u32x4*>(ks + (32 * (2 * s + half) + r32) * 16));
         };
@@ -641,7 +646,7 @@ void prefill_kernel(PrefillArgs a) {
           for (int rb = 0; rb < kRowBlocks; ++rb) o[rb][db] = mfma_32x32x16(va, pf[rb][tt], o[rb][db]);
         }
       }
-      if constexpr (kRel) {
+      if constexpr (kPin) {
         // V fragments (two transposing reads each) read two MFMAs ahead, pinned likewise.
         __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4, 1);
 #pragma unroll
@@ -672,9 +677,9 @@ void prefill_kernel(PrefillArgs a) {
     step(std::integral_constant<int, 2>{}, kt);
     if (++kt > kt_hi) break;
   }
-  // Full layers: the last step's reloads may still be in flight; done before the workgroup
-  // ends.
-  if constexpr (!T::kWindowed) wait_vmcnt<0>();
+  // The last step's reloads may still be in flight: done before the epilogue (which stages
+  // through the ring on sliding layers) and before the workgroup ends.
+  if constexpr (!T::kWindowed || kPin) wait_vmcnt<0>();
 
   // ---- epilogue: O / l * sigmoid(gate), bf16
   if constexpr (T::kWindowed) {
