@@ -794,7 +794,7 @@ def main():
                 "bound": "mfma", "achieved": r["full_call_tflops"], "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": r["full_call_tflops"] / PEAK_BF16_TFLOPS,
                 "traffic": measured_traffic("prefill_full_s32768"),
-                "kernel": "full-layer attention call at S=32768 (prefill_rope_kernel<1> + prefill_kernel<1, false>)",
+                "kernel": "full-layer attention call at S=32768 (prefill_rope_kernel<1, true> + prefill_kernel<1, false>)",
                 "flop_per_launch": r["full_flop_per_call"], "ms_per_launch": r["full_call_ms"]}
             configs["stack36_prefill_s32768"] = r
         elif name in ("full_s8192", "sliding_s1024"):

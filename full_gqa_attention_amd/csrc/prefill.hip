@@ -202,7 +202,12 @@ __device__ __forceinline__ void issue_one(const PrefillArgs& a, int b, const Seq
         const int n = kKLoads * wave + i;
         dma16_s((const uint8_t*)a.k_rot + base, kswz_src(n, lane, lim), ks + n * 1024);
       } else {
-        const uint8_t* src = (const uint8_t*)a.k_rot + base + 64 * wave;
+        // Wave w loads dims 32w .. 32w + 31 of the tile's keys: rotated ones from the
+        // workspace, the rest (full layers: dims >= 64, which RoPE leaves as they are)
+        // straight from K, so that the RoPE pass writes only the rotated dims.
+        constexpr int kRot = LayerTraits<LT>::kRot;
+        const bool rotated = kRot == kHeadDim || wave < kRot / 32;   // wave-uniform
+        const uint8_t* src = (const uint8_t*)(rotated ? a.k_rot : a.k) + base + 64 * wave;
         dma16_s(src, (uint32_t)(min(l31, lim) * 2048 + 16 * h + 32 * i), ks + (kKLoads * wave + i) * 1024);
       }
     } else {
@@ -248,11 +253,15 @@ __device__ __forceinline__ void issue_tile(const PrefillArgs& a, int b, const Se
 // Spark-X2.6-4B-Base hybrid attention explainer, eliteato.com/news/34565, sections
 // "全局注意力 5M 基频 RoPE" and "滑动窗口 512".  One thread per 16-byte chunk of a K row: a
 // rotary chunk also reads its partner chunk (dims + or - r/2) and computes its own half of
-// the pair.
-template <int LT>
+// the pair.  Full layers without a prefix read dims >= r straight from K in the attention,
+// so the pass writes only the rotated chunks of k_rot; with ROT_ONLY (no cache either) it
+// has one thread per rotated chunk only.
+template <int LT, bool ROT_ONLY = false>
 __global__ __launch_bounds__(256) void prefill_rope_kernel(PrefillArgs a) {
   using T = LayerTraits<LT>;
+  static_assert(!ROT_ONLY || LT == kFull, "sliding layers rotate every dim");
   constexpr int kHalf = T::kRot / 16;                // chunks in the first half of the rotary span
+  constexpr int kRowChunks = ROT_ONLY ? 2 * kHalf : 32;   // threads per K row
   __shared__ double s_inv[T::kRot / 2];
   if (threadIdx.x < T::kRot / 2) s_inv[threadIdx.x] = rope_inv_rev(threadIdx.x, T::kRot, log2(T::kTheta));
   __syncthreads();
@@ -261,9 +270,10 @@ __global__ __launch_bounds__(256) void prefill_rope_kernel(PrefillArgs a) {
   // Grid: x = tokens of a sequence (two per workgroup), y = sequence.
   const int b = blockIdx.y;
   const SeqSpan sp = seq_span(a, b);
-  const int t = (int)((blockIdx.x * blockDim.x + threadIdx.x) >> 7);   // token within the sequence
-  const int g = (threadIdx.x >> 5) & 3;
-  const int c = threadIdx.x & 31;
+  const int idx = (int)(blockIdx.x * blockDim.x + threadIdx.x);
+  const int t = idx / (kKvHeads * kRowChunks);       // token within the sequence
+  const int g = (idx / kRowChunks) % kKvHeads;
+  const int c = idx % kRowChunks;
   if (t >= sp.len) return;
   const size_t row = (sp.row0 + t) * kKvHeads + g;
   const int p = a.start_pos + t;
@@ -285,7 +295,7 @@ __global__ __launch_bounds__(256) void prefill_rope_kernel(PrefillArgs a) {
                    : pack_bf16x2(a0 * c0 + b0 * s0, a1 * c1 + b1 * s1);
     }
   }
-  st_global16(a.k_rot + row * kHeadDim + 8 * c, y);
+  if (LT == kSliding || a.start_pos > 0 || c < 2 * kHalf) st_global16(a.k_rot + row * kHeadDim + 8 * c, y);
   if (a.cache_k != nullptr && (LT == kFull || (a.start_pos == 0 && t >= sp.len - kWindow))) {
     const int slot = LT == kFull ? p : (p & (kWindow - 1));
     const size_t dst = (((size_t)b * a.cache_cap + slot) * kKvHeads + g) * kHeadDim + 8 * c;
@@ -1223,7 +1233,13 @@ hipError_t launch_prefill(int layer_type, const PrefillArgs& a, hipStream_t stre
       hipLaunchKernelGGL(prefill_ring_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, a);
     }
   } else {
-    hipLaunchKernelGGL(prefill_rope_kernel<kFull>, rope_grid, dim3(256), 0, stream, a);
+    if (a.start_pos == 0 && a.cache_k == nullptr) {
+      constexpr int kRotChunks = LayerTraits<kFull>::kRot / 8;     // rotated 16-byte chunks per row
+      const dim3 grid((unsigned)(((size_t)a.seq_len * kKvHeads * kRotChunks + 255) / 256), (unsigned)a.batch);
+      hipLaunchKernelGGL((prefill_rope_kernel<kFull, true>), grid, dim3(256), 0, stream, a);
+    } else {
+      hipLaunchKernelGGL(prefill_rope_kernel<kFull>, rope_grid, dim3(256), 0, stream, a);
+    }
     if (a.start_pos > 0)
       hipLaunchKernelGGL((prefill_kernel<kFull, true>), dim3(blocks), dim3(kThreads), 0, stream, a);
     else
