@@ -337,7 +337,9 @@ __device__ __forceinline__ void block_coords(int id, int batch, int nqb, int& b,
     const int r = 8 / units;
     const int x = id & 7, j = id >> 3;
     unit = x / r;
-    qidx = r * j + (x % r);
+    // Full layers deal each run of r blocks in alternating directions (snake order), so
+    // that the XCDs sharing a unit get equal work (blocks of a full layer differ in size).
+    qidx = r * j + (LT == kFull && (j & 1) ? r - 1 - x % r : x % r);
   } else {
     unit = id % units;
     qidx = id / units;
