@@ -13,8 +13,10 @@
 //
 // K/V tiles of 32 keys stream through a 3-stage LDS ring filled by direct global->LDS
 // loads (no register staging), issued two tiles ahead:
-//   * K tile (already rotated), chunk-major (16-byte chunk c of key j at slot 32c + j): the
-//     MFMA A operand of S^T = K Q^T is one conflict-free 16-byte read.
+//   * K tile (rotated dims from the workspace; on full layers the dims RoPE leaves alone
+//     straight from K), chunk-major (16-byte chunk c of key j at slot 32c + j): the MFMA A
+//     operand of S^T = K Q^T is one conflict-free 16-byte read.  Without a prefix the K and
+//     V fragment reads are pinned ahead of their MFMAs (K four, V two).
 //   * V tile, row-major with the chunk index XOR-swizzled by 4 * (row % 4): the A operand
 //     of O^T += V^T P^T (V transposed) comes from two ds_read_b64_tr_b16 per MFMA, which
 //     transpose 16-bit elements across each group of 16 lanes.
@@ -22,7 +24,8 @@
 //     query row per block, so softmax statistics need no broadcast.  Q is rotated and
 //     pre-scaled by log2(e)/16 once; the softmax runs in exp2 form in fp32; the running
 //     maximum moves only when a score exceeds it by more than 8 (P <= 2^8), so the O
-//     rescale is rare; row sums come from v_dot2_f32_bf16 on the rounded P.
+//     rescale is rare (full layers start the QK MFMAs from minus that maximum); row sums
+//     come from v_dot2_f32_bf16 on the rounded P.
 // Sliding layers visit only the 512-key band (Spark-X2.6-4B-Base hybrid attention
 // explainer, eliteato.com/news/34565, section "滑动窗口 512"); full layers every earlier
 // key (section "36 层混合注意力排布").  Epilogue: O / l * sigmoid(gate) (F16 vs Q4

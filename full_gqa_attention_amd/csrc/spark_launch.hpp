@@ -11,7 +11,8 @@ struct PrefillArgs {
   const uint16_t* q;      // [T, 16, 256]: T = B * S tokens, or the sum of the lengths (varlen)
   const uint16_t* k;      // [T, 4, 256]
   const uint16_t* v;      // [T, 4, 256]
-  uint16_t* k_rot;        // [T, 4, 256] workspace: K after RoPE
+  uint16_t* k_rot;        // [T, 4, 256] workspace: K after RoPE (full layers without a
+                          // prefix: only the rotated dims, the rest is read from k)
   const uint16_t* gate;   // [T, 16]
   uint16_t* out;          // [T, 16, 256]
   uint16_t* cache_k;      // [B, cap, 4, 256] or null
