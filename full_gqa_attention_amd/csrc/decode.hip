@@ -158,6 +158,11 @@ __device__ __forceinline__ void attend_segment(const DecodeArgs& a, int b, int L
 #pragma unroll
       for (int i = 0; i < 8; ++i)
         *reinterpret_cast<u32x4*>(s_k8 + (4 * i + (lane >> 4)) * kK8Pitch + 16 * (lane & 15)) = kg[i];
+      // Other lanes of this wave read these rows next, and the next chunk overwrites them
+      // after this one's reads.  The rows belong to this wave alone, and LDS executes one
+      // wave's operations in issue order, so a write is in LDS before any later read of the
+      // wave and a read has its data before any later write; the wave barrier only keeps the
+      // compiler from moving the accesses across it.
       __builtin_amdgcn_wave_barrier();
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
